@@ -1,0 +1,216 @@
+"""Python binding of the crkv C ABI (``include/crkv.h``).
+
+Argument marshalling only: every step of the attention, impact and top-k path
+runs in the HIP kernels of ``libcrkv.so``. torch supplies device memory and
+the current stream; nothing here computes. If the library has not been built
+the import of a function raises; there is no fallback.
+
+Functions carry the C names:
+
+* ``crkv_attn_chunks(Q, chunk_K, chunk_V, chunk_len, m, q_len, H, H_kv, d, out, impact, ...)``
+* ``crkv_attn_chunks_batched(problems, H, H_kv, d, ...)``
+* ``crkv_topk(impact, n, k, idx, ...)`` and ``crkv_topk_batched(...)``
+* ``crkv_budget(n_doc, r)``, ``crkv_workspace_size(...)``, ``crkv_version()``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcrkv.so")
+
+CRKV_OK = 0
+CRKV_E_INVAL = -1
+CRKV_E_UNSUPPORTED = -2
+CRKV_E_HIP = -3
+CRKV_E_NOMEM = -4
+CRKV_F32 = 0
+CRKV_BF16 = 1
+MODES = {"query": 0, "cross": 1, "all": 2}
+
+
+class CrkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("crkv status %d: %s" % (status, message))
+        self.status = status
+
+
+class crkv_opts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("mode", ctypes.c_int), ("stream", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("timing_events", ctypes.c_void_p * 2)]
+
+
+class crkv_problem(ctypes.Structure):
+    _fields_ = [("Q", ctypes.c_void_p), ("chunk_K", ctypes.POINTER(ctypes.c_void_p)),
+                ("chunk_V", ctypes.POINTER(ctypes.c_void_p)),
+                ("chunk_len", ctypes.POINTER(ctypes.c_int32)), ("m", ctypes.c_int),
+                ("q_len", ctypes.c_int), ("out", ctypes.c_void_p), ("impact", ctypes.c_void_p)]
+
+
+_lib = None
+
+DECLARED = ["crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
+            "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_status_string",
+            "crkv_last_error", "crkv_version"]
+
+
+def lib():
+    """The loaded libcrkv.so (torch is imported first so that the library
+    binds to the same HIP runtime as torch's tensors and streams)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libcrkv.so is not built: run `python -m attention_precomputed_chunk_amd.build`")
+        try:
+            import torch  # noqa: F401  (shares its HIP runtime with the library)
+        except ImportError:
+            pass
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+        L.crkv_opts_init.argtypes = [ctypes.POINTER(crkv_opts)]
+        L.crkv_opts_init.restype = None
+        L.crkv_attn_chunks.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i32),
+                                       c_int, c_int, c_int, c_int, c_int, vp, vp,
+                                       ctypes.POINTER(crkv_opts)]
+        L.crkv_attn_chunks.restype = c_int
+        L.crkv_attn_chunks_batched.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                               ctypes.POINTER(crkv_opts)]
+        L.crkv_attn_chunks_batched.restype = c_int
+        L.crkv_topk.argtypes = [vp, c_int, c_int, vp, ctypes.POINTER(crkv_opts)]
+        L.crkv_topk.restype = c_int
+        L.crkv_topk_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                        ctypes.POINTER(vp), c_int, ctypes.POINTER(crkv_opts)]
+        L.crkv_topk_batched.restype = c_int
+        L.crkv_budget.argtypes = [ctypes.c_int64, ctypes.c_double]
+        L.crkv_budget.restype = ctypes.c_int64
+        L.crkv_workspace_size.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                          ctypes.POINTER(crkv_opts)]
+        L.crkv_workspace_size.restype = ctypes.c_size_t
+        L.crkv_status_string.argtypes = [c_int]
+        L.crkv_status_string.restype = ctypes.c_char_p
+        L.crkv_last_error.argtypes = []
+        L.crkv_last_error.restype = ctypes.c_char_p
+        L.crkv_version.argtypes = []
+        L.crkv_version.restype = c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != CRKV_OK:
+        raise CrkvError(status, lib().crkv_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CRKV_BF16
+    if t.dtype == torch.float32:
+        return CRKV_F32
+    raise TypeError("Q must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def make_opts(dtype: int = CRKV_F32, mode: str = "query", stream=None, workspace=None,
+              workspace_bytes: int = 0, timing_events=None) -> crkv_opts:
+    o = crkv_opts()
+    lib().crkv_opts_init(ctypes.byref(o))
+    o.dtype = dtype
+    o.mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    o.stream = stream or None
+    o.workspace = _ptr(workspace)
+    o.workspace_bytes = int(workspace_bytes)
+    if timing_events is not None:
+        o.timing_events[0] = timing_events[0]
+        o.timing_events[1] = timing_events[1]
+    return o
+
+
+class _Problem:
+    """Keeps the ctypes arrays of one crkv_problem alive."""
+
+    def __init__(self, Q, chunk_K, chunk_V, chunk_len, q_len, out, impact):
+        m = len(chunk_len) - 1
+        if len(chunk_K) != m + 1 or len(chunk_V) != m + 1:
+            raise ValueError("chunk_K, chunk_V and chunk_len need m + 1 entries")
+        self.k = (ctypes.c_void_p * (m + 1))(*[_ptr(x) for x in chunk_K])
+        self.v = (ctypes.c_void_p * (m + 1))(*[_ptr(x) for x in chunk_V])
+        self.lens = (ctypes.c_int32 * (m + 1))(*[int(x) for x in chunk_len])
+        self.c = crkv_problem(_ptr(Q), self.k, self.v, self.lens, m, int(q_len), _ptr(out), _ptr(impact))
+
+
+def crkv_attn_chunks(Q, chunk_K: Sequence, chunk_V: Sequence, chunk_len: Sequence[int], m: int,
+                     q_len: int, H: int, H_kv: int, d: int, out, impact, mode: str = "query",
+                     stream=None, workspace=None, workspace_bytes: int = 0, timing_events=None,
+                     dtype: Optional[int] = None):
+    p = _Problem(Q, chunk_K, chunk_V, chunk_len, q_len, out, impact)
+    if p.c.m != m:
+        raise ValueError("m = %d but chunk_len has %d entries" % (m, len(chunk_len)))
+    o = make_opts(_dtype_code(Q) if dtype is None else dtype, mode, stream, workspace,
+                  workspace_bytes, timing_events)
+    _check(lib().crkv_attn_chunks(p.c.Q, p.k, p.v, p.lens, m, int(q_len), H, H_kv, d,
+                                  p.c.out, p.c.impact, ctypes.byref(o)))
+
+
+def _problems(problems):
+    ps = [_Problem(pr["Q"], pr["chunk_K"], pr["chunk_V"], pr["chunk_len"], pr["q_len"], pr["out"],
+                   pr["impact"]) for pr in problems]
+    arr = (crkv_problem * len(ps))(*[p.c for p in ps])
+    return ps, arr
+
+
+def crkv_attn_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int,
+                             mode: str = "query", stream=None, workspace=None,
+                             workspace_bytes: int = 0, timing_events=None,
+                             dtype: Optional[int] = None):
+    """problems: dicts with keys Q, chunk_K, chunk_V, chunk_len, q_len, out, impact."""
+    keep, arr = _problems(problems)
+    o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream,
+                  workspace, workspace_bytes, timing_events)
+    _check(lib().crkv_attn_chunks_batched(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+def crkv_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: str = "query",
+                        dtype: Optional[int] = None) -> int:
+    keep, arr = _problems(problems)
+    o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream=0)
+    return int(lib().crkv_workspace_size(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+def crkv_topk(impact, n: int, k: int, idx, stream=None):
+    o = make_opts(stream=stream)
+    _check(lib().crkv_topk(_ptr(impact), int(n), int(k), _ptr(idx), ctypes.byref(o)))
+
+
+def crkv_topk_batched(impacts: Sequence, ns: Sequence[int], ks: Sequence[int], idxs: Sequence,
+                      stream=None):
+    P = len(impacts)
+    ip = (ctypes.c_void_p * P)(*[_ptr(x) for x in impacts])
+    nn = (ctypes.c_int32 * P)(*[int(x) for x in ns])
+    kk = (ctypes.c_int32 * P)(*[int(x) for x in ks])
+    xp = (ctypes.c_void_p * P)(*[_ptr(x) for x in idxs])
+    o = make_opts(stream=stream)
+    _check(lib().crkv_topk_batched(ip, nn, kk, xp, P, ctypes.byref(o)))
+
+
+def crkv_budget(n_doc: int, r: float) -> int:
+    return int(lib().crkv_budget(int(n_doc), float(r)))
+
+
+def crkv_version() -> int:
+    return int(lib().crkv_version())

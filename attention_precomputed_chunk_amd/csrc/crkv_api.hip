@@ -1,0 +1,583 @@
+// Host side of the crkv C ABI: argument validation, the per-call plan
+// (segment table, key tiles, work items, impact-partial slots), the upload of
+// that plan through a pinned staging ring, and the kernel launches.
+//
+// Nothing here synchronises the caller's stream. The only host waits are on
+// staging-ring events, which complete once an earlier call's table upload
+// has been consumed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "crkv.h"
+#include "crkv_internal.h"
+
+namespace crkv {
+hipError_t launch_attn(bool bf16, int d, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
+hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
+hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream);
+}  // namespace crkv
+
+using namespace crkv;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(e == hipErrorOutOfMemory ? CRKV_E_NOMEM : CRKV_E_HIP, "%s: %s", what,
+                hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------ pinned staging ring
+// Plan tables are written into pinned host memory and copied to the device
+// on the caller's stream. A slot is reused only after the event recorded
+// behind its copy has completed.
+struct StagingRing {
+    static constexpr int kSlots = 8;
+    struct Slot {
+        void *host = nullptr;
+        size_t cap = 0;
+        hipEvent_t ev = nullptr;
+        bool pending = false;
+    };
+    std::mutex mu;
+    Slot slots[kSlots];
+    int next = 0;
+};
+
+std::mutex g_rings_mu;
+std::map<int, std::unique_ptr<StagingRing>> g_rings;
+
+StagingRing *ring_for_device(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_rings_mu);
+    auto &r = g_rings[dev];
+    if (!r)
+        r.reset(new StagingRing());
+    return r.get();
+}
+
+// Copies `bytes` from `src` to device `dst` on `stream` through the ring.
+int staged_upload(void *dst, const void *src, size_t bytes, hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    StagingRing *ring = ring_for_device(dev);
+    std::lock_guard<std::mutex> lk(ring->mu);
+    StagingRing::Slot &s = ring->slots[ring->next];
+    ring->next = (ring->next + 1) % StagingRing::kSlots;
+    if (s.pending) {
+        e = hipEventSynchronize(s.ev);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventSynchronize(staging)");
+        s.pending = false;
+    }
+    if (!s.ev) {
+        e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipEventCreate(staging)");
+    }
+    if (s.cap < bytes) {
+        if (s.host)
+            (void)hipHostFree(s.host);
+        s.host = nullptr;
+        s.cap = 0;
+        const size_t cap = std::max<size_t>(align_up(bytes, 65536), 65536);
+        e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipHostMalloc(staging)");
+        s.cap = cap;
+    }
+    memcpy(s.host, src, bytes);
+    e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(plan)");
+    e = hipEventRecord(s.ev, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipEventRecord(staging)");
+    s.pending = true;
+    return CRKV_OK;
+}
+
+// ------------------------------------------------------------ scratch
+struct Scratch {
+    void *ptr = nullptr;
+    bool owned = false;
+};
+
+int scratch_get(Scratch &sc, size_t bytes, const crkv_opts &o, hipStream_t stream)
+{
+    if (o.workspace) {
+        if (o.workspace_bytes < bytes)
+            return fail(CRKV_E_INVAL, "workspace too small: %zu bytes given, %zu needed",
+                        o.workspace_bytes, bytes);
+        if (reinterpret_cast<uintptr_t>(o.workspace) & 255u)
+            return fail(CRKV_E_INVAL, "workspace must be 256-byte aligned");
+        sc.ptr = o.workspace;
+        sc.owned = false;
+        return CRKV_OK;
+    }
+    hipError_t e = hipMallocAsync(&sc.ptr, std::max<size_t>(bytes, 256), stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMallocAsync(scratch)");
+    sc.owned = true;
+    return CRKV_OK;
+}
+
+void scratch_release(Scratch &sc, hipStream_t stream)
+{
+    if (sc.owned && sc.ptr)
+        (void)hipFreeAsync(sc.ptr, stream);
+    sc.ptr = nullptr;
+    sc.owned = false;
+}
+
+// ------------------------------------------------------------ validation
+int check_opts(const crkv_opts &o)
+{
+    if (o.dtype != CRKV_F32 && o.dtype != CRKV_BF16)
+        return fail(CRKV_E_INVAL, "opts.dtype %d is not CRKV_F32 or CRKV_BF16", o.dtype);
+    if (o.mode < CRKV_IMPACT_QUERY_ROWS || o.mode > CRKV_IMPACT_ALL_ROWS)
+        return fail(CRKV_E_INVAL, "opts.mode %d is not a crkv_mode", o.mode);
+    if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u))
+        return fail(CRKV_E_INVAL, "workspace must be 256-byte aligned");
+    return CRKV_OK;
+}
+
+int check_problem(const crkv_problem &p, int idx, int H, int H_kv, int d, int mode)
+{
+    if (!p.Q || !p.out || !p.impact)
+        return fail(CRKV_E_INVAL, "problem %d: Q, out and impact must be non-null", idx);
+    if (!p.chunk_K || !p.chunk_V || !p.chunk_len)
+        return fail(CRKV_E_INVAL, "problem %d: chunk_K, chunk_V and chunk_len must be non-null", idx);
+    if (p.m < 0)
+        return fail(CRKV_E_INVAL, "problem %d: m = %d < 0", idx, p.m);
+    if (p.q_len < 1)
+        return fail(CRKV_E_INVAL, "problem %d: q_len = %d < 1", idx, p.q_len);
+    if (p.chunk_len[p.m] != p.q_len)
+        return fail(CRKV_E_INVAL, "problem %d: chunk_len[m] = %d must equal q_len = %d", idx,
+                    p.chunk_len[p.m], p.q_len);
+    int64_t n = 0;
+    for (int c = 0; c <= p.m; ++c) {
+        const int32_t len = p.chunk_len[c];
+        if (len < 0)
+            return fail(CRKV_E_INVAL, "problem %d: chunk_len[%d] = %d < 0", idx, c, len);
+        if (len > 0 && (!p.chunk_K[c] || !p.chunk_V[c]))
+            return fail(CRKV_E_INVAL, "problem %d: chunk %d has %d keys but a null K or V", idx, c, len);
+        if (len > 0 && (!aligned16(p.chunk_K[c]) || !aligned16(p.chunk_V[c])))
+            return fail(CRKV_E_INVAL, "problem %d: chunk %d K/V must be 16-byte aligned", idx, c);
+        n += len;
+    }
+    if (n >= (int64_t)1 << 30)
+        return fail(CRKV_E_UNSUPPORTED, "problem %d: %lld keys exceed 2^30", idx, (long long)n);
+    const int64_t rows = mode == CRKV_IMPACT_QUERY_ROWS ? p.q_len : n;
+    if (rows * (int64_t)H * d >= (int64_t)1 << 40 || rows * (int64_t)(H / H_kv) >= (int64_t)1 << 30)
+        return fail(CRKV_E_UNSUPPORTED, "problem %d: too many rows", idx);
+    if (!aligned16(p.Q) || !aligned16(p.out))
+        return fail(CRKV_E_INVAL, "problem %d: Q and out must be 16-byte aligned", idx);
+    if (reinterpret_cast<uintptr_t>(p.impact) & 3u)
+        return fail(CRKV_E_INVAL, "problem %d: impact must be 4-byte aligned", idx);
+    return CRKV_OK;
+}
+
+int check_shape(int n_problems, int H, int H_kv, int d)
+{
+    if (n_problems < 1)
+        return fail(CRKV_E_INVAL, "n_problems = %d < 1", n_problems);
+    if (H < 1 || H_kv < 1)
+        return fail(CRKV_E_INVAL, "H = %d and H_kv = %d must be >= 1", H, H_kv);
+    if (H % H_kv != 0)
+        return fail(CRKV_E_INVAL, "H = %d is not a multiple of H_kv = %d", H, H_kv);
+    if (d != 64 && d != 128)
+        return fail(CRKV_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", d);
+    return CRKV_OK;
+}
+
+// ------------------------------------------------------------ plan
+struct Plan {
+    std::vector<ProbDesc> probs;
+    std::vector<SegDesc> segs;
+    std::vector<KTile> tiles;
+    std::vector<int32_t> slot_end;
+    std::vector<ItemDesc> items;
+    std::vector<size_t> seg_base, tile_base, slot_base, partial_base;   // per problem
+    size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0;
+    size_t table_bytes = 0, off_partial = 0, total_bytes = 0;
+    int max_keys = 0;
+};
+
+// Builds the plan for a validated batch. Work items are ordered so that the
+// row blocks of one (problem, KV head) land on the same XCD (workgroup i runs
+// on XCD i % 8) next to each other in dispatch order, and so share their K/V
+// reads through that XCD's L2; groups are dealt to XCDs longest first.
+void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, int H_kv,
+                const crkv_opts &o)
+{
+    const int G = H / H_kv;
+    const bool bf16 = o.dtype == CRKV_BF16;
+    const int cap = bf16 ? kWaves * kRowTilesBf16 : 1;
+    struct Group {
+        int64_t cost;
+        std::vector<ItemDesc> items;
+    };
+    std::vector<Group> groups;
+    size_t partial_floats = 0;
+    pl.probs.resize(n_problems);
+    for (int pi = 0; pi < n_problems; ++pi) {
+        const crkv_problem &p = problems[pi];
+        int32_t n_doc = 0;
+        for (int c = 0; c < p.m; ++c)
+            n_doc += p.chunk_len[c];
+        const int32_t N = n_doc + p.q_len;
+        const bool query = o.mode == CRKV_IMPACT_QUERY_ROWS;
+        const int32_t rows = query ? p.q_len : N;
+        const int32_t pos0 = query ? n_doc : 0;
+        pl.seg_base.push_back(pl.segs.size());
+        pl.tile_base.push_back(pl.tiles.size());
+        int32_t start = 0;
+        for (int c = 0; c <= p.m; ++c) {
+            const int32_t len = p.chunk_len[c];
+            pl.segs.push_back(SegDesc{p.chunk_K[c], p.chunk_V[c], len, start});
+            for (int32_t t = 0; t < len; t += kKeyTile)
+                pl.tiles.push_back(KTile{c, t, std::min(kKeyTile, len - t), start + t});
+            start += len;
+        }
+        const KTile *ptiles = pl.tiles.data() + pl.tile_base.back();
+        const int n_tiles = (int)(pl.tiles.size() - pl.tile_base.back());
+        const int64_t packed = (int64_t)G * rows;
+        const int nrt = (int)((packed + kRowTile - 1) / kRowTile);
+        const int nblk = (nrt + cap - 1) / cap;
+        const int n_slots = H_kv * nblk;
+        pl.slot_base.push_back(pl.slot_end.size());
+        pl.slot_end.resize(pl.slot_end.size() + n_slots, 0);
+        pl.partial_base.push_back(partial_floats);
+        partial_floats += align_up((size_t)n_slots * N, 64);
+        ProbDesc &pd = pl.probs[pi];
+        memset(&pd, 0, sizeof pd);
+        pd.n_tiles = n_tiles;
+        pd.n_seg = p.m + 1;
+        pd.n_doc = n_doc;
+        pd.n_keys = N;
+        pd.rows = rows;
+        pd.pos0 = pos0;
+        pd.n_slots = n_slots;
+        pl.max_keys = std::max(pl.max_keys, (int)N);
+        for (int kv = 0; kv < H_kv; ++kv) {
+            Group g;
+            g.cost = 0;
+            for (int b = 0; b < nblk; ++b) {
+                const int tb = (int)((int64_t)b * nrt / nblk);
+                const int te = (int)((int64_t)(b + 1) * nrt / nblk);
+                const int64_t last_row = std::min<int64_t>(packed, (int64_t)te * kRowTile) - 1;
+                const int64_t key_end = pos0 + last_row / G + 1;
+                int n_kt = 0;
+                while (n_kt < n_tiles && ptiles[n_kt].key0 < key_end)
+                    ++n_kt;
+                const int slot = kv * nblk + b;
+                pl.slot_end[pl.slot_base.back() + slot] =
+                    n_kt ? ptiles[n_kt - 1].key0 + ptiles[n_kt - 1].n_valid : 0;
+                ItemDesc it{};
+                it.prob = pi;
+                it.kv_head = kv;
+                it.tile_begin = tb;
+                it.n_rowtiles = te - tb;
+                it.n_ktiles = n_kt;
+                it.slot = slot;
+                g.cost += (int64_t)(te - tb) * std::max(n_kt, 1);
+                g.items.push_back(it);
+            }
+            groups.push_back(std::move(g));
+        }
+    }
+    std::stable_sort(groups.begin(), groups.end(),
+                     [](const Group &x, const Group &y) { return x.cost > y.cost; });
+    constexpr int kXcd = 8;
+    std::vector<std::vector<ItemDesc>> q(kXcd);
+    std::vector<int64_t> load(kXcd, 0);
+    for (auto &g : groups) {
+        int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+        for (auto &it : g.items)
+            q[x].push_back(it);
+        load[x] += g.cost;
+    }
+    size_t depth = 0;
+    for (auto &v : q)
+        depth = std::max(depth, v.size());
+    ItemDesc empty{};   // n_rowtiles = 0: the workgroup exits at once
+    for (size_t d = 0; d < depth; ++d)
+        for (int x = 0; x < kXcd; ++x)
+            pl.items.push_back(d < q[x].size() ? q[x][d] : empty);
+    // trim trailing empties
+    while (!pl.items.empty() && pl.items.back().n_rowtiles == 0)
+        pl.items.pop_back();
+
+    pl.off_probs = 0;
+    pl.off_items = align_up(pl.off_probs + pl.probs.size() * sizeof(ProbDesc), 256);
+    pl.off_segs = align_up(pl.off_items + pl.items.size() * sizeof(ItemDesc), 256);
+    pl.off_tiles = align_up(pl.off_segs + pl.segs.size() * sizeof(SegDesc), 256);
+    pl.off_slots = align_up(pl.off_tiles + pl.tiles.size() * sizeof(KTile), 256);
+    pl.table_bytes = align_up(pl.off_slots + pl.slot_end.size() * sizeof(int32_t), 256);
+    pl.off_partial = pl.table_bytes;
+    pl.total_bytes = pl.off_partial + partial_floats * sizeof(float);
+}
+
+// Writes the plan tables (with device addresses inside `dev`) into `host`.
+void fill_tables(Plan &pl, const crkv_problem *problems, unsigned char *host, unsigned char *dev)
+{
+    for (size_t pi = 0; pi < pl.probs.size(); ++pi) {
+        ProbDesc &pd = pl.probs[pi];
+        pd.Q = problems[pi].Q;
+        pd.out = problems[pi].out;
+        pd.impact = problems[pi].impact;
+        pd.partial = reinterpret_cast<float *>(dev + pl.off_partial) + pl.partial_base[pi];
+        pd.tiles = reinterpret_cast<const KTile *>(dev + pl.off_tiles) + pl.tile_base[pi];
+        pd.segs = reinterpret_cast<const SegDesc *>(dev + pl.off_segs) + pl.seg_base[pi];
+        pd.slot_end = reinterpret_cast<const int32_t *>(dev + pl.off_slots) + pl.slot_base[pi];
+    }
+    memset(host, 0, pl.table_bytes);
+    memcpy(host + pl.off_probs, pl.probs.data(), pl.probs.size() * sizeof(ProbDesc));
+    memcpy(host + pl.off_items, pl.items.data(), pl.items.size() * sizeof(ItemDesc));
+    memcpy(host + pl.off_segs, pl.segs.data(), pl.segs.size() * sizeof(SegDesc));
+    memcpy(host + pl.off_tiles, pl.tiles.data(), pl.tiles.size() * sizeof(KTile));
+    memcpy(host + pl.off_slots, pl.slot_end.data(), pl.slot_end.size() * sizeof(int32_t));
+}
+
+crkv_opts resolve(const crkv_opts *opts)
+{
+    crkv_opts o;
+    crkv_opts_init(&o);
+    if (opts)
+        o = *opts;
+    return o;
+}
+
+int validate_batch(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                   const crkv_opts &o)
+{
+    int rc = check_opts(o);
+    if (rc)
+        return rc;
+    rc = check_shape(n_problems, H, H_kv, d);
+    if (rc)
+        return rc;
+    if (!problems)
+        return fail(CRKV_E_INVAL, "problems must be non-null");
+    for (int i = 0; i < n_problems; ++i) {
+        rc = check_problem(problems[i], i, H, H_kv, d, o.mode);
+        if (rc)
+            return rc;
+    }
+    return CRKV_OK;
+}
+
+int check_topk_args(const float *impact, int n, int k, const int32_t *idx, int which)
+{
+    if (!impact || !idx)
+        return fail(CRKV_E_INVAL, "top-k %d: impact and idx must be non-null", which);
+    if (n < 1)
+        return fail(CRKV_E_INVAL, "top-k %d: n = %d < 1", which, n);
+    if (k < 1 || k > n)
+        return fail(CRKV_E_INVAL, "top-k %d: k = %d outside [1, n = %d]", which, k, n);
+    if (k > kTopkMaxK)
+        return fail(CRKV_E_UNSUPPORTED, "top-k %d: k = %d exceeds %d", which, k, kTopkMaxK);
+    if ((reinterpret_cast<uintptr_t>(impact) & 3u) || (reinterpret_cast<uintptr_t>(idx) & 3u))
+        return fail(CRKV_E_INVAL, "top-k %d: impact and idx must be 4-byte aligned", which);
+    return CRKV_OK;
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+
+extern "C" {
+
+void crkv_opts_init(crkv_opts *opts)
+{
+    if (!opts)
+        return;
+    memset(opts, 0, sizeof *opts);
+    opts->dtype = CRKV_F32;
+    opts->mode = CRKV_IMPACT_QUERY_ROWS;
+}
+
+int crkv_version(void) { return CRKV_VERSION; }
+
+const char *crkv_last_error(void) { return g_last_error.c_str(); }
+
+const char *crkv_status_string(int status)
+{
+    switch (status) {
+    case CRKV_OK: return "ok";
+    case CRKV_E_INVAL: return "invalid argument";
+    case CRKV_E_UNSUPPORTED: return "unsupported configuration";
+    case CRKV_E_HIP: return "HIP runtime error";
+    case CRKV_E_NOMEM: return "out of memory";
+    default: return "unknown status";
+    }
+}
+
+int64_t crkv_budget(int64_t n_doc, double r)
+{
+    if (n_doc < 0 || !(r >= 0.0 && r <= 1.0))
+        return -1;
+    const double x = std::floor(r * (double)n_doc);
+    const int64_t k = (int64_t)x;
+    return k < 1 ? 1 : k;
+}
+
+size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                           const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    if (validate_batch(problems, n_problems, H, H_kv, d, o) != CRKV_OK)
+        return 0;
+    Plan pl;
+    build_plan(pl, problems, n_problems, H, H_kv, o);
+    return pl.total_bytes;
+}
+
+int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                             const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = validate_batch(problems, n_problems, H, H_kv, d, o);
+    if (rc)
+        return rc;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    Plan pl;
+    build_plan(pl, problems, n_problems, H, H_kv, o);
+
+    Scratch sc;
+    rc = scratch_get(sc, pl.total_bytes, o, stream);
+    if (rc)
+        return rc;
+    unsigned char *dev = static_cast<unsigned char *>(sc.ptr);
+    std::vector<unsigned char> host(pl.table_bytes);
+    fill_tables(pl, problems, host.data(), dev);
+    rc = staged_upload(dev, host.data(), pl.table_bytes, stream);
+    if (rc) {
+        scratch_release(sc, stream);
+        return rc;
+    }
+    AttnArgs args{};
+    args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
+    args.items = reinterpret_cast<const ItemDesc *>(dev + pl.off_items);
+    args.H = H;
+    args.H_kv = H_kv;
+    args.G = H / H_kv;
+    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
+    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+
+    hipError_t e = hipSuccess;
+    if (o.timing_events[0])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
+    if (e == hipSuccess)
+        e = launch_attn(o.dtype == CRKV_BF16, d, args, (int)pl.items.size(), stream);
+    if (e == hipSuccess && o.timing_events[1])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    if (e == hipSuccess)
+        e = launch_combine(args.probs, n_problems, pl.max_keys, stream);
+    scratch_release(sc, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "attention launch");
+    return CRKV_OK;
+}
+
+int crkv_attn_chunks(const void *Q, const void *const *chunk_K, const void *const *chunk_V,
+                     const int32_t *chunk_len, int m, int q_len, int H, int H_kv, int d, void *out,
+                     float *impact, const crkv_opts *opts)
+{
+    crkv_problem p;
+    p.Q = Q;
+    p.chunk_K = chunk_K;
+    p.chunk_V = chunk_V;
+    p.chunk_len = chunk_len;
+    p.m = m;
+    p.q_len = q_len;
+    p.out = out;
+    p.impact = impact;
+    return crkv_attn_chunks_batched(&p, 1, H, H_kv, d, opts);
+}
+
+int crkv_topk(const float *impact, int n, int k, int32_t *idx, const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = check_topk_args(impact, n, k, idx, 0);
+    if (rc)
+        return rc;
+    TopkDesc td{impact, idx, n, k};
+    hipError_t e = launch_topk_one(td, reinterpret_cast<hipStream_t>(o.stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "top-k launch");
+    return CRKV_OK;
+}
+
+int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_t *k,
+                      int32_t *const *idx, int n_problems, const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    if (n_problems < 1)
+        return fail(CRKV_E_INVAL, "n_problems = %d < 1", n_problems);
+    if (!impact || !n || !k || !idx)
+        return fail(CRKV_E_INVAL, "impact, n, k and idx arrays must be non-null");
+    if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u))
+        return fail(CRKV_E_INVAL, "workspace must be 256-byte aligned");
+    std::vector<TopkDesc> descs(n_problems);
+    for (int i = 0; i < n_problems; ++i) {
+        int rc = check_topk_args(impact[i], n[i], k[i], idx[i], i);
+        if (rc)
+            return rc;
+        descs[i] = TopkDesc{impact[i], idx[i], n[i], k[i]};
+    }
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    if (n_problems == 1) {
+        hipError_t e = launch_topk_one(descs[0], stream);
+        return e == hipSuccess ? CRKV_OK : hip_fail(e, "top-k launch");
+    }
+    const size_t bytes = align_up(descs.size() * sizeof(TopkDesc), 256);
+    Scratch sc;
+    int rc = scratch_get(sc, bytes, o, stream);
+    if (rc)
+        return rc;
+    std::vector<unsigned char> host(bytes, 0);
+    memcpy(host.data(), descs.data(), descs.size() * sizeof(TopkDesc));
+    rc = staged_upload(sc.ptr, host.data(), bytes, stream);
+    if (rc) {
+        scratch_release(sc, stream);
+        return rc;
+    }
+    hipError_t e = launch_topk_batched(static_cast<const TopkDesc *>(sc.ptr), n_problems, stream);
+    scratch_release(sc, stream);
+    return e == hipSuccess ? CRKV_OK : hip_fail(e, "top-k launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Descriptors shared by the host planner and the gfx950 kernels.
+//
+// A call is planned on the host into three device tables, uploaded with one
+// copy: per problem (ProbDesc), per segment (SegDesc), per key tile (KTile)
+// and per work item (ItemDesc). Key tiles never straddle a segment, so a tile
+// has one base pointer and contiguous keys; the last tile of a segment is
+// partial and its missing keys are masked.
+#pragma once
+#include <stdint.h>
+
+namespace crkv {
+
+constexpr int kWaves = 4;          // waves per workgroup (one per SIMD)
+constexpr int kThreads = kWaves * 64;
+constexpr int kKeyTile = 64;       // keys staged per LDS tile
+constexpr int kRowTile = 16;       // rows per MFMA row tile
+constexpr int kRowTilesBf16 = 5;   // row tiles per wave, bf16 kernels (5 x (16 Q + 32 O) registers fit in 512 without spills)
+constexpr int kRowTilesF32 = 4;    // row tiles per wave, fp32 kernels
+constexpr int kTopkMaxK = 8192;    // selection buffer held in LDS
+
+struct SegDesc {
+    const void *K;      // [H_kv][len][d]
+    const void *V;
+    int32_t len;
+    int32_t start;      // position of the segment's first key
+};
+
+struct KTile {
+    int32_t seg;        // segment index within the problem
+    int32_t local0;     // first key of the tile inside the segment
+    int32_t n_valid;    // keys present (<= kKeyTile)
+    int32_t key0;       // global position of the tile's first key
+};
+
+struct ProbDesc {
+    const void *Q;          // [H][rows][d]
+    void *out;              // [H][rows][d]
+    float *partial;         // [n_slots][n_keys] impact partials
+    const KTile *tiles;     // key tiles in key order
+    const SegDesc *segs;    // n_seg = m + 1 segments
+    const int32_t *slot_end;// per slot: keys [0, slot_end) were written
+    float *impact;          // [n_keys]
+    int32_t n_tiles;
+    int32_t n_seg;
+    int32_t n_doc;
+    int32_t n_keys;
+    int32_t rows;           // rows per head
+    int32_t pos0;           // position of row 0 (N_doc in query-row mode, else 0)
+    int32_t n_slots;
+    int32_t pad;
+};
+
+struct ItemDesc {
+    int32_t prob;
+    int32_t kv_head;
+    int32_t tile_begin;     // first packed 16-row tile (rows packed as (j, h) within the group)
+    int32_t n_rowtiles;     // <= kWaves * row tiles per wave
+    int32_t n_ktiles;       // key tiles visited (prefix of the problem's list)
+    int32_t slot;           // impact partial slot within the problem
+    int32_t pad0, pad1;
+};
+
+struct AttnArgs {
+    const ProbDesc *probs;
+    const ItemDesc *items;
+    int32_t H, H_kv, G;
+    int32_t cross;          // 1: impact skips rows of the key's own segment
+    float c_log2;           // log2(e) / sqrt(d)
+};
+
+struct TopkDesc {
+    const float *value;
+    int32_t *idx;
+    int32_t n, k;
+};
+
+}  // namespace crkv

@@ -1,0 +1,160 @@
+/*
+ * crkv: attention of a query block over precomputed per-chunk K/V caches,
+ * CacheBlend impact, and top-k selection, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (TurboRAG summary, "Precomputing the KV cache" and the causal
+ * attention equation; CacheBlend summary, "Mathematical formulation", the
+ * Impact equation and the selective-recompute listing):
+ *
+ *   K = Concat(K^(1), ..., K^(m), K^(Q)),  V likewise (query block last),
+ *   out = softmax(Q K^T / sqrt(d) + M) V,
+ *   impact[i] = sum over heads h and counted rows j of softmax weight p_{h,j,i},
+ *   idx = the k = max(1, floor(r * N_doc)) largest impact[0..N_doc).
+ *
+ * M is causal over the concatenated sequence: the key at position i is
+ * visible to the row at position p iff i <= p. For query rows (positions
+ * N_doc + j) this is "causal only inside the query block".
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers are owned by the caller; the library never frees or
+ *    retains them. Host arrays (the chunk pointer tables, lengths, problem
+ *    lists) are read during the call only and may be freed when it returns.
+ *  - Work is enqueued asynchronously on opts->stream (a hipStream_t; NULL
+ *    means the null stream). No call synchronises the stream. A kernel fault
+ *    surfaces at the caller's next synchronisation.
+ *  - Every argument is validated before anything is enqueued. Failures return
+ *    a negative crkv_status and never abort; crkv_last_error() gives the
+ *    reason (per thread).
+ *  - Segment c of a problem stores K and V as [H_kv][chunk_len[c]][d],
+ *    contiguous, in the element type opts->dtype. Entries 0..m-1 are document
+ *    chunks (length 0 allowed: the chunk is skipped); entry m is the query
+ *    block's own K/V and must have length q_len. Chunks are never copied or
+ *    concatenated in memory: the library reads them through the pointer table.
+ *  - Q and out are [H][rows][d] in opts->dtype. rows = q_len in
+ *    CRKV_IMPACT_QUERY_ROWS mode, and N_doc + q_len (every position of the
+ *    concatenated sequence) in the two all-position modes.
+ *  - Query head h reads KV head h / (H / H_kv).
+ *  - impact is float32 [N_doc + q_len] (document keys first, then the query
+ *    block's keys), overwritten, summed over all H query heads.
+ *  - Supported: d in {64, 128}; H % H_kv == 0; N_doc + q_len < 2^31.
+ */
+#ifndef CRKV_H
+#define CRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CRKV_VERSION 1
+
+typedef enum {
+    CRKV_OK = 0,
+    CRKV_E_INVAL = -1,       /* an argument is out of its documented range */
+    CRKV_E_UNSUPPORTED = -2, /* valid, but outside what the kernels handle  */
+    CRKV_E_HIP = -3,         /* a HIP runtime call or launch failed          */
+    CRKV_E_NOMEM = -4        /* device or pinned host allocation failed      */
+} crkv_status;
+
+typedef enum { CRKV_F32 = 0, CRKV_BF16 = 1 } crkv_dtype;
+
+/*
+ * Which rows are attended and which rows count towards impact.
+ *  QUERY_ROWS: the q_len query rows; impact sums all of them (CacheBlend
+ *              listing: softmax over all keys, column sum over query rows).
+ *  CROSS_DOC:  every position is a row (full causal prefill of
+ *              [D_1; ...; D_m; q]); impact of key i sums only rows j whose
+ *              segment differs from key i's segment (CacheBlend Impact
+ *              equation, index set read as doc(j) != doc(i); the query block
+ *              is segment m). Same-segment rows still take part in softmax.
+ *  ALL_ROWS:   every position is a row; impact sums every row (a check mode:
+ *              the impact vector then sums to (N_doc + q_len) * H).
+ */
+typedef enum {
+    CRKV_IMPACT_QUERY_ROWS = 0,
+    CRKV_IMPACT_CROSS_DOC = 1,
+    CRKV_IMPACT_ALL_ROWS = 2
+} crkv_mode;
+
+typedef struct crkv_opts {
+    int dtype;              /* crkv_dtype of Q, K, V and out                   */
+    int mode;               /* crkv_mode                                        */
+    void *stream;           /* hipStream_t, NULL = null stream                  */
+    void *workspace;        /* device scratch, or NULL: the library allocates
+                               and frees it stream-ordered on `stream`          */
+    size_t workspace_bytes; /* size of `workspace`; see crkv_workspace_size     */
+    void *timing_events[2]; /* optional hipEvent_t pair recorded on `stream`
+                               immediately before and after the attention
+                               kernel (for measuring that kernel alone)         */
+} crkv_opts;
+
+/* Defaults: fp32, query-row mode, null stream, library-managed scratch. */
+void crkv_opts_init(crkv_opts *opts);
+
+/*
+ * Attention of one problem over m document chunks plus the query block.
+ *  Q          device, [H][rows][d]
+ *  chunk_K/V  host arrays of m + 1 device pointers (see conventions)
+ *  chunk_len  host array of m + 1 lengths; chunk_len[m] == q_len
+ *  out        device, [H][rows][d], written
+ *  impact     device, float32 [N_doc + q_len], written
+ *  opts       NULL for the defaults
+ */
+int crkv_attn_chunks(const void *Q, const void *const *chunk_K, const void *const *chunk_V,
+                     const int32_t *chunk_len, int m, int q_len, int H, int H_kv, int d,
+                     void *out, float *impact, const crkv_opts *opts);
+
+/*
+ * Top-k selection (CacheBlend listing's topk over the document slice of the
+ * impact vector): the k largest of impact[0..n) by float32 order (-0 < +0),
+ * ties broken by the lower index, written to idx[0..k) sorted by (value
+ * descending, index ascending). Requires 1 <= k <= n and k <= 8192; NaN
+ * inputs are outside the contract.
+ *  impact  device float32 [n]; idx device int32 [k], written.
+ */
+int crkv_topk(const float *impact, int n, int k, int32_t *idx, const crkv_opts *opts);
+
+/* One problem of a batch (a layer, or a request). Pointer fields as in
+ * crkv_attn_chunks; chunk_K/chunk_V/chunk_len are host arrays. */
+typedef struct crkv_problem {
+    const void *Q;
+    const void *const *chunk_K;
+    const void *const *chunk_V;
+    const int32_t *chunk_len;
+    int m;
+    int q_len;
+    void *out;
+    float *impact;
+} crkv_problem;
+
+/* All problems of a batch (shared H, H_kv, d, dtype and mode; each with its
+ * own chunks, lengths and q_len) in one attention launch. */
+int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv,
+                             int d, const crkv_opts *opts);
+
+/* Top-k for n_problems vectors in one launch. impact and idx are host arrays
+ * of device pointers; n and k are host arrays. Same contract as crkv_topk. */
+int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_t *k,
+                      int32_t *const *idx, int n_problems, const crkv_opts *opts);
+
+/* Recompute budget k = max(1, floor(r * n_doc)) (CacheBlend: r times the
+ * summed document lengths; the listing's max(1, int(N_doc * r))). Computed
+ * in double. Returns -1 if n_doc < 0 or r is not in [0, 1]. */
+int64_t crkv_budget(int64_t n_doc, double r);
+
+/* Bytes of device scratch a crkv_attn_chunks_batched call with these
+ * arguments needs when the caller passes opts->workspace (256-byte aligned
+ * pointer). Returns 0 if the arguments are invalid. */
+size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                           const crkv_opts *opts);
+
+const char *crkv_status_string(int status);
+const char *crkv_last_error(void);
+int crkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CRKV_H */

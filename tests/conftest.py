@@ -18,3 +18,13 @@ def _oracle_built():
     import oracle
     oracle.build(force=False)
     yield
+
+
+@pytest.fixture(scope="session")
+def crkv_lib():
+    """The HIP library, built in-tree if no build is present."""
+    import attention_precomputed_chunk_amd as crkv
+    from attention_precomputed_chunk_amd import build as crkv_build
+    if not os.path.exists(crkv.LIB_PATH):
+        crkv_build.build()
+    return crkv.lib()

@@ -1,0 +1,132 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/crkv.h declares, and rejects invalid arguments with status codes
+before anything is enqueued (no device is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_precomputed_chunk_amd as crkv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "crkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(crkv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(crkv_lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(crkv_lib, n), n
+    assert set(names) == set(crkv.DECLARED)
+
+
+def test_version_and_status_strings(crkv_lib):
+    assert crkv.crkv_version() == 1
+    assert crkv_lib.crkv_status_string(0) == b"ok"
+    assert crkv_lib.crkv_status_string(-1) == b"invalid argument"
+    assert crkv_lib.crkv_status_string(-2) == b"unsupported configuration"
+    assert crkv_lib.crkv_status_string(-3) == b"HIP runtime error"
+    assert crkv_lib.crkv_status_string(-4) == b"out of memory"
+
+
+def test_budget(crkv_lib):
+    assert crkv.crkv_budget(128, 0.1) == 12
+    assert crkv.crkv_budget(2048, 0.1) == 204
+    assert crkv.crkv_budget(10000, 0.15) == 1500
+    assert crkv.crkv_budget(8192, 0.05) == 409
+    assert crkv.crkv_budget(3, 0.1) == 1
+    assert crkv.crkv_budget(-1, 0.1) == -1
+    assert crkv.crkv_budget(10, 1.5) == -1
+
+
+FAKE = 0x10000   # aligned, never dereferenced: validation fails first
+
+
+def _call(Q=FAKE, K=None, V=None, lens=(64, 64, 16), q_len=16, H=4, H_kv=4, d=64, out=FAKE,
+          impact=FAKE, dtype=crkv.CRKV_F32, mode=0, workspace=None):
+    L = crkv.lib()
+    m = len(lens) - 1
+    K = K if K is not None else [FAKE] * (m + 1)
+    V = V if V is not None else [FAKE] * (m + 1)
+    ka = (ctypes.c_void_p * (m + 1))(*K)
+    va = (ctypes.c_void_p * (m + 1))(*V)
+    la = (ctypes.c_int32 * (m + 1))(*lens)
+    o = crkv.crkv_opts()
+    L.crkv_opts_init(ctypes.byref(o))
+    o.dtype = dtype
+    o.mode = mode
+    o.workspace = workspace
+    rc = L.crkv_attn_chunks(Q, ka, va, la, m, q_len, H, H_kv, d, out, impact, ctypes.byref(o))
+    return rc, L.crkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(Q=None), -1, "non-null"),
+    (dict(out=None), -1, "non-null"),
+    (dict(impact=None), -1, "non-null"),
+    (dict(H=6, H_kv=4), -1, "multiple"),
+    (dict(H=0), -1, ">= 1"),
+    (dict(d=96), -2, "d = 96"),
+    (dict(lens=(64, 64, 15)), -1, "q_len"),
+    (dict(lens=(64, -3, 16)), -1, "< 0"),
+    (dict(q_len=0, lens=(64, 0)), -1, "q_len"),
+    (dict(K=[FAKE, 0, FAKE]), -1, "null K or V"),
+    (dict(V=[FAKE, FAKE + 8, FAKE]), -1, "aligned"),
+    (dict(Q=FAKE + 4), -1, "aligned"),
+    (dict(impact=FAKE + 2), -1, "aligned"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(mode=5), -1, "mode"),
+    (dict(workspace=FAKE + 16), -1, "256-byte"),
+])
+def test_attn_rejects_invalid_arguments(crkv_lib, kwargs, status, needle):
+    rc, msg = _call(**kwargs)
+    assert rc == status, msg
+    assert needle in msg
+
+
+def test_zero_length_chunk_with_null_pointer_is_allowed_by_validation(crkv_lib):
+    # a zero-length document chunk may have null K/V; the call then fails only
+    # later, at the first HIP call, when there is no GPU -- so check the size query
+    probs = (crkv.crkv_problem * 1)()
+    k = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    v = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    lens = (ctypes.c_int32 * 3)(64, 0, 16)
+    probs[0] = crkv.crkv_problem(FAKE, k, v, lens, 2, 16, FAKE, FAKE)
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    assert crkv_lib.crkv_workspace_size(probs, 1, 4, 4, 64, ctypes.byref(o)) > 0
+    o.dtype = 9
+    assert crkv_lib.crkv_workspace_size(probs, 1, 4, 4, 64, ctypes.byref(o)) == 0
+
+
+def test_topk_rejects_invalid_arguments(crkv_lib):
+    L = crkv_lib
+    o = crkv.crkv_opts()
+    L.crkv_opts_init(ctypes.byref(o))
+    assert L.crkv_topk(None, 10, 3, FAKE, ctypes.byref(o)) == -1
+    assert L.crkv_topk(FAKE, 10, 0, FAKE, ctypes.byref(o)) == -1
+    assert L.crkv_topk(FAKE, 10, 11, FAKE, ctypes.byref(o)) == -1
+    assert L.crkv_topk(FAKE, 0, 1, FAKE, ctypes.byref(o)) == -1
+    assert L.crkv_topk(FAKE, 100000, 9000, FAKE, ctypes.byref(o)) == -2
+    assert L.crkv_topk(FAKE + 2, 10, 3, FAKE, ctypes.byref(o)) == -1
+    P = 2
+    ip = (ctypes.c_void_p * P)(FAKE, FAKE)
+    nn = (ctypes.c_int32 * P)(10, 10)
+    kk = (ctypes.c_int32 * P)(3, 12)
+    xp = (ctypes.c_void_p * P)(FAKE, FAKE)
+    assert L.crkv_topk_batched(ip, nn, kk, xp, P, ctypes.byref(o)) == -1
+    assert "top-k 1" in L.crkv_last_error().decode()
+    assert L.crkv_topk_batched(ip, nn, kk, xp, 0, ctypes.byref(o)) == -1
+
+
+def test_batched_rejects_empty_batch(crkv_lib):
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    assert crkv_lib.crkv_attn_chunks_batched(None, 0, 4, 4, 64, ctypes.byref(o)) == -1
+    assert crkv_lib.crkv_attn_chunks_batched(None, 1, 4, 4, 64, ctypes.byref(o)) == -1

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs. Small shapes are compared element by
+element; the full-size workloads run in the launch configuration the bench
+times and are compared on oracle-computable samples plus invariants."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import attention_precomputed_chunk_amd as crkv  # noqa: E402
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from gpu_util import (DEV, DeviceWorkload, check_impact, check_out, check_selection,  # noqa: E402
+                      to_host)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(crkv_lib):
+    yield
+
+
+def check_sorted_selection(idx, imp_doc, label=""):
+    """The GPU output order is (value desc, index asc) on its own impact."""
+    v = imp_doc[idx]
+    assert np.all(v[:-1] >= v[1:]), "%s not sorted by value" % label
+    ties = v[:-1] == v[1:]
+    assert np.all(idx[:-1][ties] < idx[1:][ties]), "%s ties not in index order" % label
+
+
+def run_and_compare(wl, problems=None, label="", oracle_rows=None):
+    """Launch the whole workload once, then compare the listed problems (all
+    by default) with the oracle. Returns the device workload."""
+    dw = DeviceWorkload(wl)
+    dw.attn()
+    gidx = dw.topk()
+    torch.cuda.synchronize()
+    sel = range(len(wl.problems)) if problems is None else problems
+    for pi in sel:
+        prob = wl.problems[pi]
+        lab = "%s[problem %d]" % (label, pi)
+        out_ref, imp_ref, _ = oracle.attn(prob, wl.H, wl.H_kv, wl.d, wl.dtype, wl.mode)
+        d = dw.problems[pi]
+        check_out(to_host(d["out"]), out_ref, wl.dtype, lab)
+        imp = d["impact"].cpu().numpy()
+        check_impact(imp, imp_ref, lab)
+        n_doc = prob.n_doc
+        if n_doc:
+            k = oracle.budget(n_doc, wl.r)
+            ref_idx = oracle.topk(imp_ref[:n_doc].astype(np.float32), k)
+            g = gidx[pi].cpu().numpy()
+            check_selection(g, ref_idx, imp_ref[:n_doc], lab)
+            check_sorted_selection(g, imp[:n_doc], lab)
+            # bit-exact selection when both sides sort the same fp32 vector
+            exact = torch.from_numpy(imp_ref[:n_doc].astype(np.float32)).to(DEV)
+            out_idx = torch.full((k,), -1, dtype=torch.int32, device=DEV)
+            crkv.crkv_topk(exact, n_doc, k, out_idx)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(out_idx.cpu().numpy(), ref_idx)
+    return dw
+
+
+# ------------------------------------------------------------------ small shapes, full compare
+
+SMALL = [
+    # seed, doc_lens, q, H, H_kv, d, dtype, mode
+    (1, [130, 67, 0, 5], 37, 8, 2, 128, "bf16", "query"),
+    (2, [64, 64], 16, 4, 4, 64, "bf16", "query"),
+    (3, [200, 1, 63], 100, 4, 1, 128, "bf16", "query"),
+    (4, [100, 77, 64], 20, 4, 4, 128, "bf16", "cross"),
+    (5, [33, 91], 19, 6, 2, 64, "bf16", "cross"),
+    (6, [70, 70], 12, 2, 2, 128, "bf16", "all"),
+    (7, [], 45, 4, 2, 128, "bf16", "query"),
+    (8, [511, 2], 1, 8, 8, 128, "bf16", "query"),
+    (9, [65, 0, 130], 70, 16, 2, 128, "bf16", "query"),
+    (10, [96, 31], 9, 4, 2, 128, "f32", "query"),
+    (11, [64, 64], 16, 4, 4, 64, "f32", "cross"),
+    (12, [17, 40], 23, 3, 1, 64, "f32", "all"),
+    (13, [0, 0, 300], 3, 2, 2, 64, "f32", "query"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_shapes(case):
+    seed, doc, q, H, H_kv, d, dtype, mode = SMALL[case]
+    say("small case", SMALL[case])
+    wl = workloads.custom(100 + seed, doc, q, H, H_kv, d, dtype=dtype, mode=mode, r=0.1,
+                          n_problems=2)
+    run_and_compare(wl, label="small%d" % case)
+
+
+def test_tiny_config():
+    """1 layer, 4 heads, d=64, fp32; 2 chunks x 64 + 16 query rows; top-12."""
+    say("tiny")
+    wl = workloads.generate("tiny")
+    run_and_compare(wl, label="tiny")
+
+
+def test_llama2_layer_config():
+    """32 heads MHA, d=128, bf16; 4 x 512 + 64 query rows; top-204."""
+    say("llama2_7b_layer")
+    wl = workloads.generate("llama2_7b_layer")
+    run_and_compare(wl, label="llama2")
+
+
+def test_llama3_gqa_32_layers():
+    """32 layers in one launch (the benchmarked call); layers 0, 17, 31
+    against the oracle, impact mass of every layer."""
+    say("llama3_8b_gqa_32l: generate")
+    wl = workloads.generate("llama3_8b_gqa_32l")
+    say("llama3_8b_gqa_32l: launch + compare")
+    dw = run_and_compare(wl, problems=[0, 17, 31], label="llama3")
+    for pi, d in enumerate(dw.problems):
+        imp = d["impact"].double().sum().item()
+        assert abs(imp - wl.problems[pi].q_len * wl.H) < 1e-4 * wl.problems[pi].q_len * wl.H
+
+
+def test_llama3_gqa_iid_keys():
+    """The other reading of 'same distributions as config 1': iid N(0,1) K."""
+    say("llama3_8b_gqa_32l iid K")
+    wl = workloads.generate("llama3_8b_gqa_32l", problems=[0, 1], k_outliers=0)
+    run_and_compare(wl, label="llama3-iid")
+
+
+def test_ragged_batch():
+    """16 requests, 64 query / 8 KV heads; requests 0, 7, 15 against the oracle."""
+    say("ragged_70b")
+    wl = workloads.generate("ragged_70b")
+    dw = run_and_compare(wl, problems=[0, 7, 15], label="ragged")
+    for pi, d in enumerate(dw.problems):
+        want = wl.problems[pi].q_len * wl.H
+        assert abs(d["impact"].double().sum().item() - want) < 1e-4 * want
+
+
+def test_cross_doc_config():
+    """Every position is a row (8 x 1024 + 128). Keys at positions >= 7680
+    have an exact oracle from the rows at positions >= 7680; sampled early
+    rows check the output; the all-rows launch checks the impact mass."""
+    say("cross_doc")
+    wl = workloads.generate("cross_doc")
+    dw = DeviceWorkload(wl)
+    dw.attn()
+    gidx = dw.topk()
+    torch.cuda.synchronize()
+    prob = wl.problems[0]
+    d = dw.problems[0]
+    out = to_host(d["out"])
+    imp = d["impact"].cpu().numpy()
+    r0 = 7680
+    out_ref, imp_ref, _ = oracle.attn(prob, wl.H, wl.H_kv, wl.d, wl.dtype, "cross", row_lo=r0)
+    check_out(out[:, r0:], out_ref[:, r0:], "bf16", "cross late rows")
+    check_impact(imp[r0:], imp_ref[r0:], "cross late keys")
+    for lo in (0, 1000, 4090, 6143):
+        o_ref, _, _ = oracle.attn(prob, wl.H, wl.H_kv, wl.d, wl.dtype, "cross", row_lo=lo,
+                                  row_hi=lo + 16)
+        check_out(out[:, lo:lo + 16], o_ref[:, lo:lo + 16], "bf16", "cross rows %d" % lo)
+    assert len(set(gidx[0].cpu().numpy().tolist())) == oracle.budget(prob.n_doc, wl.r)
+    # all-rows mode: impact sums to N * H and bounds the cross-document impact
+    wl_all = workloads.Workload(spec=None, H=wl.H, H_kv=wl.H_kv, d=wl.d, dtype=wl.dtype, mode="all",
+                                r=wl.r, problems=wl.problems)
+    dw_all = DeviceWorkload(wl_all)
+    dw_all.attn()
+    torch.cuda.synchronize()
+    imp_all = dw_all.problems[0]["impact"].cpu().numpy().astype(np.float64)
+    assert abs(imp_all.sum() - prob.n_keys * wl.H) < 1e-4 * prob.n_keys * wl.H
+    np.testing.assert_array_equal(to_host(dw_all.problems[0]["out"]), out)
+    assert np.all(imp <= imp_all * (1 + 1e-5) + 1e-30)
+
+
+# ------------------------------------------------------------------ behaviour
+
+def test_repeat_calls_are_bit_identical():
+    wl = workloads.custom(21, [300, 129], 50, 8, 2, 128, dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.attn()
+    torch.cuda.synchronize()
+    o1 = dw.problems[0]["out"].clone()
+    i1 = dw.problems[0]["impact"].clone()
+    for _ in range(3):
+        dw.attn()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.problems[0]["out"], o1)
+        assert torch.equal(dw.problems[0]["impact"], i1)
+
+
+def test_workspace_and_stream():
+    wl = workloads.custom(22, [150, 90], 33, 4, 2, 128, dtype="bf16", mode="cross")
+    dw = DeviceWorkload(wl)
+    dw.attn()
+    torch.cuda.synchronize()
+    o1 = dw.problems[0]["out"].clone()
+    i1 = dw.problems[0]["impact"].clone()
+    nbytes = crkv.crkv_workspace_size(dw.problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    assert nbytes > 0
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=DEV)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dw.problems[0]["out"].zero_()
+        dw.problems[0]["impact"].zero_()
+        dw.attn(stream=s, workspace=aligned, workspace_bytes=nbytes)
+    s.synchronize()
+    assert torch.equal(dw.problems[0]["out"], o1)
+    assert torch.equal(dw.problems[0]["impact"], i1)
+    with pytest.raises(crkv.CrkvError):
+        dw.attn(workspace=aligned, workspace_bytes=nbytes - 256)
+
+
+def test_partition_of_keys_into_chunks():
+    """The same keys split into different chunks give the same attention
+    (within tolerance: tile boundaries move)."""
+    wl = workloads.custom(23, [256, 128], 40, 8, 2, 128, dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.attn()
+    torch.cuda.synchronize()
+    out_a = to_host(dw.problems[0]["out"])
+    imp_a = dw.problems[0]["impact"].cpu().numpy().astype(np.float64)
+    p = wl.problems[0]
+    Kc = np.concatenate(p.K[:-1], axis=1)
+    Vc = np.concatenate(p.V[:-1], axis=1)
+    cuts = [0, 1, 65, 65, 200, 384]
+    K = [np.ascontiguousarray(Kc[:, a:b]) for a, b in zip(cuts[:-1], cuts[1:])] + [p.K[-1]]
+    V = [np.ascontiguousarray(Vc[:, a:b]) for a, b in zip(cuts[:-1], cuts[1:])] + [p.V[-1]]
+    lens = [b - a for a, b in zip(cuts[:-1], cuts[1:])] + [p.q_len]
+    p2 = workloads.Problem(K=K, V=V, lens=lens, q_len=p.q_len, Q=p.Q)
+    wl2 = workloads.Workload(spec=None, H=wl.H, H_kv=wl.H_kv, d=wl.d, dtype=wl.dtype, mode=wl.mode,
+                             r=wl.r, problems=[p2])
+    dw2 = DeviceWorkload(wl2)
+    dw2.attn()
+    torch.cuda.synchronize()
+    check_out(to_host(dw2.problems[0]["out"]), out_a, "bf16", "repartition")
+    check_impact(dw2.problems[0]["impact"].cpu().numpy(), imp_a, "repartition")
+
+
+# ------------------------------------------------------------------ top-k alone
+
+@pytest.mark.parametrize("n,k,kind", [
+    (1, 1, "normal"), (8, 8, "normal"), (1000, 1, "normal"), (10000, 1500, "normal"),
+    (16384, 1638, "normal"), (5000, 700, "ties"), (5000, 4999, "ties"), (777, 300, "signed_zeros"),
+    (100000, 8192, "normal"), (4096, 409, "constant"), (3000, 17, "negative"),
+])
+def test_topk_bit_exact(n, k, kind):
+    rng = np.random.default_rng(n * 31 + k)
+    if kind == "normal":
+        v = rng.standard_normal(n).astype(np.float32)
+    elif kind == "ties":
+        v = rng.integers(0, 7, size=n).astype(np.float32) * np.float32(0.125)
+    elif kind == "signed_zeros":
+        v = rng.choice(np.array([-0.0, 0.0, 1e-30, -1e-30, 2.0], dtype=np.float32), size=n)
+    elif kind == "constant":
+        v = np.full(n, 0.37, dtype=np.float32)
+    else:
+        v = -np.abs(rng.standard_normal(n)).astype(np.float32)
+    ref = oracle.topk(v, k)
+    dv = torch.from_numpy(v).to(DEV)
+    idx = torch.full((k,), -1, dtype=torch.int32, device=DEV)
+    crkv.crkv_topk(dv, n, k, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_batched_matches_single():
+    rng = np.random.default_rng(5)
+    vecs = [rng.standard_normal(n).astype(np.float32) for n in (10, 999, 4096, 12000)]
+    ks = [3, 99, 409, 1200]
+    dv = [torch.from_numpy(v).to(DEV) for v in vecs]
+    idx = [torch.full((k,), -1, dtype=torch.int32, device=DEV) for k in ks]
+    crkv.crkv_topk_batched(dv, [len(v) for v in vecs], ks, idx)
+    torch.cuda.synchronize()
+    for v, k, i in zip(vecs, ks, idx):
+        np.testing.assert_array_equal(i.cpu().numpy(), oracle.topk(v, k))
