@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcrkv.so")
-SOURCES = ["crkv_api.hip", "attn.hip", "topk.hip"]
+SOURCES = ["crkv_api.hip", "attn_bf16.hip", "attn_f32.hip", "topk.hip"]
 ARCH = os.environ.get("CRKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

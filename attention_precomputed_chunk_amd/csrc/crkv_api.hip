@@ -22,7 +22,8 @@
 #include "crkv_internal.h"
 
 namespace crkv {
-hipError_t launch_attn(bool bf16, int d, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_bf16(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
 hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
 hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream);
@@ -233,18 +234,53 @@ struct Plan {
     size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0;
     size_t table_bytes = 0, off_partial = 0, total_bytes = 0;
     int max_keys = 0;
+    int rt = 1;   // row tiles per wave of the launch
 };
+
+int64_t packed_rows(const crkv_problem &p, int G, int mode)
+{
+    int64_t n = 0;
+    for (int c = 0; c <= p.m; ++c)
+        n += p.chunk_len[c];
+    return (int64_t)G * (mode == CRKV_IMPACT_QUERY_ROWS ? p.q_len : n);
+}
+
+// Row tiles per wave for a bf16 launch. Matrix and vector work of a SIMD do
+// not overlap, so a workgroup takes as long as its fullest wave: choose the
+// build that minimises sum over (problem, KV head) of blocks x RT, and on a
+// tie the larger RT (fewer workgroups re-reading the same K/V).
+int choose_rt(const crkv_problem *problems, int n_problems, int G, int mode)
+{
+    int best = kRowTileChoices[0];
+    int64_t best_cost = -1;
+    for (int rt : kRowTileChoices) {
+        if (mode == CRKV_IMPACT_CROSS_DOC && rt > kMaxRowTilesCross)
+            continue;
+        int64_t cost = 0;
+        for (int i = 0; i < n_problems; ++i) {
+            const int64_t tiles = (packed_rows(problems[i], G, mode) + kRowTile - 1) / kRowTile;
+            const int64_t blocks = (tiles + kWaves * rt - 1) / (kWaves * rt);
+            cost += blocks * rt;
+        }
+        if (best_cost < 0 || cost < best_cost || (cost == best_cost && rt > best)) {
+            best = rt;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
 
 // Builds the plan for a validated batch. Work items are ordered so that the
 // row blocks of one (problem, KV head) land on the same XCD (workgroup i runs
 // on XCD i % 8) next to each other in dispatch order, and so share their K/V
 // reads through that XCD's L2; groups are dealt to XCDs longest first.
-void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, int H_kv,
+void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                 const crkv_opts &o)
 {
     const int G = H / H_kv;
     const bool bf16 = o.dtype == CRKV_BF16;
-    const int cap = bf16 ? kWaves * kRowTilesBf16 : 1;
+    pl.rt = bf16 ? choose_rt(problems, n_problems, G, o.mode) : 1;
+    const int cap = bf16 ? kWaves * pl.rt : 1;   // row tiles per workgroup
     struct Group {
         int64_t cost;
         std::vector<ItemDesc> items;
@@ -267,8 +303,17 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
         for (int c = 0; c <= p.m; ++c) {
             const int32_t len = p.chunk_len[c];
             pl.segs.push_back(SegDesc{p.chunk_K[c], p.chunk_V[c], len, start});
-            for (int32_t t = 0; t < len; t += kKeyTile)
-                pl.tiles.push_back(KTile{c, t, std::min(kKeyTile, len - t), start + t});
+            const size_t esz = o.dtype == CRKV_BF16 ? 2 : 4;
+            for (int32_t t = 0; t < len; t += kKeyTile) {
+                KTile kt;
+                kt.K = static_cast<const unsigned char *>(p.chunk_K[c]) + (size_t)t * d * esz;
+                kt.V = static_cast<const unsigned char *>(p.chunk_V[c]) + (size_t)t * d * esz;
+                kt.n_valid = std::min(kKeyTile, len - t);
+                kt.key0 = start + t;
+                kt.seg_len = len;
+                kt.seg_lo = start;
+                pl.tiles.push_back(kt);
+            }
             start += len;
         }
         const KTile *ptiles = pl.tiles.data() + pl.tile_base.back();
@@ -295,8 +340,8 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
             Group g;
             g.cost = 0;
             for (int b = 0; b < nblk; ++b) {
-                const int tb = (int)((int64_t)b * nrt / nblk);
-                const int te = (int)((int64_t)(b + 1) * nrt / nblk);
+                const int tb = b * cap;
+                const int te = std::min(nrt, tb + cap);
                 const int64_t last_row = std::min<int64_t>(packed, (int64_t)te * kRowTile) - 1;
                 const int64_t key_end = pos0 + last_row / G + 1;
                 int n_kt = 0;
@@ -461,7 +506,7 @@ size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, 
     if (validate_batch(problems, n_problems, H, H_kv, d, o) != CRKV_OK)
         return 0;
     Plan pl;
-    build_plan(pl, problems, n_problems, H, H_kv, o);
+    build_plan(pl, problems, n_problems, H, H_kv, d, o);
     return pl.total_bytes;
 }
 
@@ -474,7 +519,7 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
         return rc;
     hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
     Plan pl;
-    build_plan(pl, problems, n_problems, H, H_kv, o);
+    build_plan(pl, problems, n_problems, H, H_kv, d, o);
 
     Scratch sc;
     rc = scratch_get(sc, pl.total_bytes, o, stream);
@@ -501,7 +546,8 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
     if (o.timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
     if (e == hipSuccess)
-        e = launch_attn(o.dtype == CRKV_BF16, d, args, (int)pl.items.size(), stream);
+        e = o.dtype == CRKV_BF16 ? launch_attn_bf16(d, pl.rt, args, (int)pl.items.size(), stream)
+                                 : launch_attn_f32(d, args, (int)pl.items.size(), stream);
     if (e == hipSuccess && o.timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
     if (e == hipSuccess)

@@ -12,9 +12,10 @@ namespace crkv {
 
 constexpr int kWaves = 4;          // waves per workgroup (one per SIMD)
 constexpr int kThreads = kWaves * 64;
-constexpr int kKeyTile = 64;       // keys staged per LDS tile
+constexpr int kKeyTile = 32;       // keys staged per LDS tile
 constexpr int kRowTile = 16;       // rows per MFMA row tile
-constexpr int kRowTilesBf16 = 5;   // row tiles per wave, bf16 kernels (5 x (16 Q + 32 O) registers fit in 512 without spills)
+constexpr int kRowTileChoices[3] = {4, 5, 7};   // row tiles per wave the bf16 kernels are built for
+constexpr int kMaxRowTilesCross = 5;            // cross-document kernels: 7 would spill
 constexpr int kRowTilesF32 = 4;    // row tiles per wave, fp32 kernels
 constexpr int kTopkMaxK = 8192;    // selection buffer held in LDS
 
@@ -25,11 +26,16 @@ struct SegDesc {
     int32_t start;      // position of the segment's first key
 };
 
+// A key tile is self-contained so that a kernel can fetch its data with a
+// single descriptor load: row `key` of KV head g lives at
+// K + (g * seg_len + key) * d elements.
 struct KTile {
-    int32_t seg;        // segment index within the problem
-    int32_t local0;     // first key of the tile inside the segment
+    const void *K;      // segment K at the tile's first key, KV head 0
+    const void *V;
     int32_t n_valid;    // keys present (<= kKeyTile)
     int32_t key0;       // global position of the tile's first key
+    int32_t seg_len;    // keys in the segment (the KV-head stride in rows)
+    int32_t seg_lo;     // global position of the segment's first key
 };
 
 struct ProbDesc {

@@ -1,0 +1,55 @@
+// Small device helpers shared by the gfx950 attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "crkv_internal.h"
+
+namespace crkv {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef short i16x4 __attribute__((__vector_size__(8)));
+typedef short i16x8 __attribute__((__vector_size__(16)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1); every lane of the
+// row receives the total.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_mov<0x128>(x);
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x122>(x);
+    x += dpp_mov<0x121>(x);
+    return x;
+}
+
+// Combine two (max, sum) softmax states; maxima are raw scores, the sums are
+// of exp2((s - max) * c).
+__device__ __forceinline__ void merge_state(float &m, float &l, float m2, float l2, float c)
+{
+    const float mn = fmaxf(m, m2);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float a = (m == -INFINITY) ? 0.f : exp2_hw((m - mu) * c);
+    const float b = (m2 == -INFINITY) ? 0.f : exp2_hw((m2 - mu) * c);
+    l = l * a + l2 * b;
+    m = mn;
+}
+
+// Segment of a position: the number of segments that end at or before it.
+__device__ __forceinline__ int segment_of(const SegDesc *segs, int n_seg, int pos)
+{
+    int s = 0;
+    for (int c = 0; c < n_seg - 1; ++c)
+        s += (segs[c].start + segs[c].len <= pos) ? 1 : 0;
+    return s;
+}
+
+}  // namespace crkv

@@ -2,13 +2,17 @@
 // selective-recompute listing: topk over the document slice of the impact,
 // k = max(1, int(N_doc * r))).
 //
-// One workgroup per vector. The fp32 values are mapped to unsigned keys that
-// order like the floats (-0 below +0). A four-pass, 8-bit radix select finds
-// the k-th largest key T. Every key above T is taken, and of the keys equal
-// to T the lowest indices are taken (an ordered scan over contiguous index
-// ranges, one per thread). The k winners are then sorted by (key descending,
-// index ascending) with a bitonic network in LDS, packed as 64-bit words
-// (key << 32 | ~index) so one descending sort does both orders.
+// One workgroup of 1024 threads per vector. The fp32 values are mapped to
+// unsigned keys that order like the floats (-0 below +0). Radix select then
+// finds the k-th largest key T, eight bits at a time, starting below the bits
+// every key shares (the common prefix of the minimum and maximum keys), so the
+// first histogram is spread over many bins even when all values have the same
+// sign and a narrow exponent range. Histograms are private per wave to keep
+// LDS atomic contention low. Every key above T is taken; of the keys equal to
+// T the lowest indices are taken (an ordered scan over contiguous index
+// ranges, one per thread). The k winners are sorted by (key descending, index
+// ascending) with a bitonic network in LDS, packed as 64-bit words
+// (key << 32 | ~index) so that one descending sort gives both orders.
 #include <hip/hip_runtime.h>
 
 #include "crkv_internal.h"
@@ -21,80 +25,147 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkLdsKeys = 16384;   // vectors up to this length are held in LDS
+
+// Inclusive prefix sum over the workgroup (every thread calls it).
+__device__ __forceinline__ int block_inclusive_scan(int x, int *wave_tot)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        wave_tot[wave] = x;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w)
+        before += wave_tot[w];
+    __syncthreads();
+    return x + before;
+}
 
 __device__ void topk_body(const TopkDesc td)
 {
-    __shared__ uint32_t hist[256];
-    __shared__ int scan[kTopkThreads];
-    __shared__ uint32_t s_digit;
-    __shared__ int s_above;
-    __shared__ int s_gt;
+    __shared__ uint32_t keys[kTopkLdsKeys];
+    __shared__ uint32_t whist[kTopkWaves][256];
     __shared__ unsigned long long sel[kTopkMaxK];
+    __shared__ int wave_tot[kTopkWaves];
+    __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_above, s_gt;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = td.n, k = td.k;
-    const float *v = td.value;
+    const bool in_lds = n <= kTopkLdsKeys;
+    auto key_at = [&](int i) -> uint32_t { return in_lds ? keys[i] : order_key(td.value[i]); };
 
-    uint32_t prefix = 0, mask = 0;
-    int remaining = k;   // how many of the keys matching `prefix` still to take
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        hist[tid] = 0;
+    // keys, and the common prefix of all of them
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = tid; i < n; i += kTopkThreads) {
+        const uint32_t kk = order_key(td.value[i]);
+        if (in_lds)
+            keys[i] = kk;
+        mn = min(mn, kk);
+        mx = max(mx, kk);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    }
+    if (lane == 0) {
+        red_min[wave] = mn;
+        red_max[wave] = mx;
+    }
+    __syncthreads();
+    mn = red_min[0];
+    mx = red_max[0];
+    for (int w = 1; w < kTopkWaves; ++w) {
+        mn = min(mn, red_min[w]);
+        mx = max(mx, red_max[w]);
+    }
+    int shift = (mn == mx) ? 0 : 32 - __clz((int)(mn ^ mx));   // bits below the common prefix
+    uint32_t pmask = shift >= 32 ? 0u : ~((1u << shift) - 1u);
+    uint32_t prefix = mn & pmask;
+    int remaining = k;   // keys still to take among those matching `prefix`
+
+    while (shift > 0) {
+        const int bits = shift >= 8 ? 8 : shift;
+        shift -= bits;
+        const uint32_t dmask = (1u << bits) - 1u;
+        for (int b = lane; b < 256; b += 64)
+            whist[wave][b] = 0;
         __syncthreads();
         for (int i = tid; i < n; i += kTopkThreads) {
-            const uint32_t key = order_key(v[i]);
-            if ((key & mask) == prefix)
-                atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            const uint32_t kk = key_at(i);
+            if ((kk & pmask) == prefix)
+                atomicAdd(&whist[wave][(kk >> shift) & dmask], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-            int cum = 0;
-            uint32_t dsel = 0;
-            for (int dg = 255; dg >= 0; --dg) {
-                const int h = (int)hist[dg];
-                if (cum + h >= remaining) {
-                    dsel = (uint32_t)dg;
-                    break;
-                }
-                cum += h;
+        if (wave == 0) {
+            // lane l owns digits 255-4l .. 252-4l (scanning from the top)
+            int c[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int dg = 255 - 4 * lane - q;
+                int h = 0;
+                for (int w = 0; w < kTopkWaves; ++w)
+                    h += (int)whist[w][dg];
+                c[q] = h;
+                tot += h;
             }
-            s_digit = dsel;
-            s_above = cum;
+            int incl = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off)
+                    incl += y;
+            }
+            int cum = incl - tot;   // keys in higher digits than this lane's first
+            const unsigned long long hit = __ballot(incl >= remaining);
+            const int first = __ffsll((long long)hit) - 1;   // lowest lane reaching `remaining`
+            if (lane == first) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (cum + c[q] >= remaining) {
+                        s_digit = (uint32_t)(255 - 4 * lane - q);
+                        s_above = cum;
+                        break;
+                    }
+                    cum += c[q];
+                }
+            }
         }
         __syncthreads();
         prefix |= s_digit << shift;
-        mask |= 255u << shift;
+        pmask |= dmask << shift;
         remaining -= s_above;
         __syncthreads();
     }
     const uint32_t T = prefix;
-    const int n_gt = k - remaining;   // keys strictly above T, all taken
+    const int n_gt = k - remaining;   // keys strictly above T: all taken
 
-    // Ordered selection of the ties: thread t scans indices [t*chunk, ...).
+    // ordered selection of the ties: thread t scans indices [t*chunk, ...)
     const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
     const int b = min(n, tid * chunk), e = min(n, b + chunk);
     int eq = 0;
     for (int i = b; i < e; ++i)
-        eq += order_key(v[i]) == T ? 1 : 0;
-    scan[tid] = eq;
+        eq += key_at(i) == T ? 1 : 0;
     if (tid == 0)
         s_gt = 0;
-    __syncthreads();
-    for (int off = 1; off < kTopkThreads; off <<= 1) {   // inclusive Hillis-Steele scan
-        const int add = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += add;
-        __syncthreads();
-    }
-    int rank = scan[tid] - eq;   // ties before this thread's range
+    int rank = block_inclusive_scan(eq, wave_tot) - eq;
     for (int i = b; i < e; ++i) {
-        const uint32_t key = order_key(v[i]);
+        const uint32_t kk = key_at(i);
         const unsigned long long packed =
-            ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
-        if (key > T) {
+            ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+        if (kk > T) {
             sel[atomicAdd(&s_gt, 1)] = packed;
-        } else if (key == T) {
+        } else if (kk == T) {
             if (rank < remaining)
                 sel[n_gt + rank] = packed;
             ++rank;
@@ -107,7 +178,7 @@ __device__ void topk_body(const TopkDesc td)
         sel[i] = 0ull;   // below every real entry
     __syncthreads();
 
-    // Bitonic sort, descending.
+    // bitonic sort, descending
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int t = tid; t < P / 2; t += kTopkThreads) {

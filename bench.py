@@ -60,7 +60,7 @@ def algorithmic_work(wl):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("attn.hip", "crkv_internal.h"):
+    for f in ("attn_bf16.hip", "device_util.h", "crkv_internal.h"):
         with open(os.path.join(ROOT, "attention_precomputed_chunk_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -51,10 +51,16 @@ class DeviceWorkload:
         return [crkv.crkv_budget(p.n_doc, self.wl.r) for p in self.wl.problems]
 
     def topk(self):
+        """Top-k over each problem's document slice (None where N_doc = 0:
+        there is nothing to select)."""
+        sel = [i for i, p in enumerate(self.wl.problems) if p.n_doc > 0]
         ks = self.budgets()
-        idx = [torch.full((k,), -1, dtype=torch.int32, device=DEV) for k in ks]
-        crkv.crkv_topk_batched([d["impact"] for d in self.problems],
-                               [p.n_doc for p in self.wl.problems], ks, idx)
+        idx = [torch.full((ks[i],), -1, dtype=torch.int32, device=DEV) if i in sel else None
+               for i in range(len(ks))]
+        if sel:
+            crkv.crkv_topk_batched([self.problems[i]["impact"] for i in sel],
+                                   [self.wl.problems[i].n_doc for i in sel], [ks[i] for i in sel],
+                                   [idx[i] for i in sel])
         return idx
 
 
@@ -63,11 +69,13 @@ def check_out(out, ref, dtype, label=""):
     if dtype == "f32":
         err = np.abs(out - ref).max()
         assert err <= 1e-5, "%s out max-abs error %.3g > 1e-5" % (label, err)
+        return float(err)
     else:
         err = np.abs(out - ref).max(axis=-1)
         scale = np.abs(ref).max(axis=-1)
         worst = (err / scale).max()
         assert worst <= 1e-2, "%s out row-relative error %.3g > 1e-2" % (label, worst)
+        return float(worst)
 
 
 def check_impact(imp, ref, label=""):
@@ -77,6 +85,7 @@ def check_impact(imp, ref, label=""):
         i = int(np.argmax(np.abs(imp - ref) / np.maximum(np.abs(ref), 1e-300)))
         raise AssertionError("%s impact: %d elements off; worst at %d: %r vs %r"
                              % (label, int(bad.sum()), i, imp[i], ref[i]))
+    return float((np.abs(imp - ref) / np.abs(ref)).max())
 
 
 def check_selection(gpu_idx, ref_idx, ref_imp_doc, label=""):

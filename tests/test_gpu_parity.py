@@ -49,9 +49,10 @@ def run_and_compare(wl, problems=None, label="", oracle_rows=None):
         lab = "%s[problem %d]" % (label, pi)
         out_ref, imp_ref, _ = oracle.attn(prob, wl.H, wl.H_kv, wl.d, wl.dtype, wl.mode)
         d = dw.problems[pi]
-        check_out(to_host(d["out"]), out_ref, wl.dtype, lab)
+        e_out = check_out(to_host(d["out"]), out_ref, wl.dtype, lab)
         imp = d["impact"].cpu().numpy()
-        check_impact(imp, imp_ref, lab)
+        e_imp = check_impact(imp, imp_ref, lab)
+        say("  %s: out err %.3g, impact rel err %.3g" % (lab, e_out, e_imp))
         n_doc = prob.n_doc
         if n_doc:
             k = oracle.budget(n_doc, wl.r)
