@@ -14,6 +14,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcrkv.so")
 SOURCES = ["crkv_api.hip", "attn_bf16.hip", "attn_f32.hip", "topk.hip"]
+# Device-code files. They never meet a NaN on the contract's inputs (masked
+# scores are -inf), so maxima need no NaN canonicalisation; and matrix-core
+# results are kept in ordinary VGPRs, which the vector ALU reads directly
+# (the default AGPR form costs a v_accvgpr_read per score).
+KERNEL_SOURCES = {"attn_bf16.hip", "attn_f32.hip", "topk.hip"}
+KERNEL_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 ARCH = os.environ.get("CRKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -21,7 +27,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -37,9 +42,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,6 +52,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        flags = HIPCC_FLAGS + (KERNEL_FLAGS if src in KERNEL_SOURCES else [])
+        _run([hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

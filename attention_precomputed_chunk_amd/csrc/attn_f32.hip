@@ -137,19 +137,38 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(const AttnArgs a)
     }
 }
 
-// impact[i] = sum over slots (fixed order) of partial[slot][i] for the slots
-// whose key range reaches i. Deterministic: no atomics anywhere.
+// impact[i] = sum over slots of partial[slot][i] for the slots whose key
+// range reaches i. One workgroup per (64 keys, problem): wave w sums slots
+// [w*S/4, (w+1)*S/4) in order, then the four wave sums are added in wave
+// order, so the result is deterministic (no atomics anywhere). Entries past a
+// slot's key range (causal row blocks end early) are never written and are
+// selected away after the load.
+constexpr int kCombineKeys = 64;
+
 __global__ void __launch_bounds__(256) impact_combine_kernel(const ProbDesc *probs)
 {
+    __shared__ float red[4][kCombineKeys];
     const ProbDesc pr = probs[blockIdx.y];
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= pr.n_keys)
+    const int k0 = blockIdx.x * kCombineKeys;
+    if (k0 >= pr.n_keys)
         return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = k0 + lane;
+    const int s_lo = (int)((int64_t)wave * pr.n_slots / 4), s_hi = (int)((int64_t)(wave + 1) * pr.n_slots / 4);
+    // Loads are unconditional (every slot row is allocated in full) and the
+    // extent test only selects, so consecutive slots' loads overlap.
+    const int ii = min(i, pr.n_keys - 1);
     float acc = 0.f;
-    for (int s = 0; s < pr.n_slots; ++s)
-        if (i < pr.slot_end[s])
-            acc += pr.partial[(size_t)s * pr.n_keys + i];
-    pr.impact[i] = acc;
+#pragma unroll 8
+    for (int s = s_lo; s < s_hi; ++s) {
+        // select on the bits: an unwritten entry may hold any pattern
+        const int v = __float_as_int(pr.partial[(size_t)s * pr.n_keys + ii]);
+        acc += __int_as_float((i < pr.slot_end[s]) ? v : 0);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && i < pr.n_keys)
+        pr.impact[i] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 // ------------------------------------------------------------------ launchers
@@ -169,7 +188,7 @@ hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipS
 {
     if (n_probs <= 0 || max_keys <= 0)
         return hipSuccess;
-    const dim3 grid((max_keys + 255) / 256, n_probs);
+    const dim3 grid((max_keys + kCombineKeys - 1) / kCombineKeys, n_probs);
     hipLaunchKernelGGL(impact_combine_kernel, grid, dim3(256), 0, stream, probs);
     return hipGetLastError();
 }

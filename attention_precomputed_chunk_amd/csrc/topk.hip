@@ -178,7 +178,11 @@ __device__ void topk_body(const TopkDesc td)
         sel[i] = 0ull;   // below every real entry
     __syncthreads();
 
-    // bitonic sort, descending
+    // Bitonic sort, descending. Thread t compares pair t (and t + 1024, ...).
+    // For strides below 64 the pairs of each 128-element block all belong to
+    // one wave, whose LDS accesses execute in order, so those stages only need
+    // a wave-level ordering point; a workgroup barrier follows every stage
+    // with a larger stride and the last stage of every size.
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int t = tid; t < P / 2; t += kTopkThreads) {
@@ -191,9 +195,16 @@ __device__ void topk_body(const TopkDesc td)
                     sel[hi] = x;
                 }
             }
-            __syncthreads();
+            if (stride >= 64 || stride == 1) {
+                __syncthreads();   // cross-wave stage, or the next size starts with one
+            } else {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
         }
     }
+    __syncthreads();
     for (int i = tid; i < k; i += kTopkThreads)
         td.idx[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(sel[i] & 0xFFFFFFFFull));
 }
