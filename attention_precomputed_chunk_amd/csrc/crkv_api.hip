@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -245,29 +246,31 @@ int64_t packed_rows(const crkv_problem &p, int G, int mode)
     return (int64_t)G * (mode == CRKV_IMPACT_QUERY_ROWS ? p.q_len : n);
 }
 
-// Row tiles per wave for a bf16 launch. Matrix and vector work of a SIMD do
-// not overlap, so a workgroup takes as long as its fullest wave: choose the
-// build that minimises sum over (problem, KV head) of blocks x RT, and on a
-// tie the larger RT (fewer workgroups re-reading the same K/V).
+// Row tiles per wave for a bf16 launch. The matrix cores and the vector ALU
+// of a SIMD do not overlap on gfx950, and a workgroup takes as long as its
+// fullest wave, so:
+//  * if every (problem, KV head) fits in one workgroup, take the smallest
+//    build that covers the largest one (least padding, K/V read once);
+//  * otherwise take kRowTilesMany, the build measured fastest when the rows
+//    of a KV head span several workgroups (ragged and cross-document
+//    workloads on MI355X).
+// CRKV_ROW_TILES forces one of the built choices (tuning experiments).
 int choose_rt(const crkv_problem *problems, int n_problems, int G, int mode)
 {
-    int best = kRowTileChoices[0];
-    int64_t best_cost = -1;
-    for (int rt : kRowTileChoices) {
-        if (mode == CRKV_IMPACT_CROSS_DOC && rt > kMaxRowTilesCross)
-            continue;
-        int64_t cost = 0;
-        for (int i = 0; i < n_problems; ++i) {
-            const int64_t tiles = (packed_rows(problems[i], G, mode) + kRowTile - 1) / kRowTile;
-            const int64_t blocks = (tiles + kWaves * rt - 1) / (kWaves * rt);
-            cost += blocks * rt;
-        }
-        if (best_cost < 0 || cost < best_cost || (cost == best_cost && rt > best)) {
-            best = rt;
-            best_cost = cost;
-        }
+    const int max_rt = mode == CRKV_IMPACT_CROSS_DOC ? kMaxRowTilesCross : 1 << 30;
+    if (const char *env = getenv("CRKV_ROW_TILES")) {
+        const int forced = atoi(env);
+        for (int rt : kRowTileChoices)
+            if (rt == forced && rt <= max_rt)
+                return rt;
     }
-    return best;
+    int64_t max_tiles = 0;
+    for (int i = 0; i < n_problems; ++i)
+        max_tiles = std::max<int64_t>(max_tiles, (packed_rows(problems[i], G, mode) + kRowTile - 1) / kRowTile);
+    for (int rt : kRowTileChoices)
+        if (rt <= max_rt && (int64_t)kWaves * rt >= max_tiles)
+            return rt;
+    return std::min(kRowTilesMany, max_rt);
 }
 
 // Builds the plan for a validated batch. Work items are ordered so that the

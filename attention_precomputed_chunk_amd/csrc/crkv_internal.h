@@ -16,6 +16,7 @@ constexpr int kKeyTile = 32;       // keys staged per LDS tile
 constexpr int kRowTile = 16;       // rows per MFMA row tile
 constexpr int kRowTileChoices[3] = {4, 5, 7};   // row tiles per wave the bf16 kernels are built for
 constexpr int kMaxRowTilesCross = 5;            // cross-document kernels: 7 would spill
+constexpr int kRowTilesMany = 5;                // when a KV head's rows span several workgroups
 constexpr int kRowTilesF32 = 4;    // row tiles per wave, fp32 kernels
 constexpr int kTopkMaxK = 8192;    // selection buffer held in LDS
 
