@@ -60,29 +60,30 @@ __device__ __forceinline__ int vswz(int key)
 // A key tile's descriptor held in scalar registers (passed by value so it is
 // never demoted to scratch memory).
 struct TileSR {
-    const uint4 *K;
-    const uint4 *V;
+    gptr<const u32x4> K;
+    gptr<const u32x4> V;
     int n_valid, key0, seg_len, seg_lo;
 };
 
-__device__ __forceinline__ const void *uniform_ptr(const void *p)
+// A descriptor is eight dwords; lane l loads dword l % 8 with a vector load,
+// one iteration before the dwords are moved to scalar registers, so the
+// load's latency is covered by a tile of work. (A scalar load would count
+// against lgkmcnt and be waited for with the next LDS read.)
+__device__ __forceinline__ uint32_t load_tile(const KTile *tiles, int i, int lane)
 {
-    const uint64_t u = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+    return as_global(reinterpret_cast<const uint32_t *>(tiles))[(size_t)i * 8 + (lane & 7)];
 }
 
-__device__ __forceinline__ TileSR fetch_tile(const KTile *tiles, int i)
+__device__ __forceinline__ TileSR to_sr(uint32_t raw)
 {
-    const KTile t = tiles[i];
+    auto dw = [&](int j) { return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)raw, j); };
     TileSR r;
-    r.K = static_cast<const uint4 *>(uniform_ptr(t.K));
-    r.V = static_cast<const uint4 *>(uniform_ptr(t.V));
-    r.n_valid = __builtin_amdgcn_readfirstlane(t.n_valid);
-    r.key0 = __builtin_amdgcn_readfirstlane(t.key0);
-    r.seg_len = __builtin_amdgcn_readfirstlane(t.seg_len);
-    r.seg_lo = __builtin_amdgcn_readfirstlane(t.seg_lo);
+    r.K = reinterpret_cast<gptr<const u32x4>>(dw(0) | (dw(1) << 32));
+    r.V = reinterpret_cast<gptr<const u32x4>>(dw(2) | (dw(3) << 32));
+    r.n_valid = (int)dw(4);
+    r.key0 = (int)dw(5);
+    r.seg_len = (int)dw(6);
+    r.seg_lo = (int)dw(7);
     return r;
 }
 
@@ -90,8 +91,8 @@ __device__ __forceinline__ TileSR fetch_tile(const KTile *tiles, int i)
 // and passed by value so that it stays in registers.
 template <int SLD>
 struct Staged {
-    uint4 k[SLD];
-    uint4 v[SLD];
+    u32x4 k[SLD];
+    u32x4 v[SLD];
 };
 
 template <int NCH, int SLD, bool WITH_V>
@@ -120,9 +121,9 @@ __device__ __forceinline__ void stage_store(const Staged<SLD> st, unsigned char 
     for (int i = 0; i < SLD; ++i) {
         const int cidx = tid + i * kThreads;
         const int key = cidx / NCH, ch = cidx % NCH;
-        *reinterpret_cast<uint4 *>(lk + key * ROW + ((ch ^ kswz<NCH>(key)) << 4)) = st.k[i];
+        *reinterpret_cast<u32x4 *>(lk + key * ROW + ((ch ^ kswz<NCH>(key)) << 4)) = st.k[i];
         if constexpr (WITH_V)
-            *reinterpret_cast<uint4 *>(lv + key * ROW + ((ch ^ vswz<NCH>(key)) << 4)) = st.v[i];
+            *reinterpret_cast<u32x4 *>(lv + key * ROW + ((ch ^ vswz<NCH>(key)) << 4)) = st.v[i];
     }
 }
 
@@ -163,10 +164,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
         const int j = r / G;
         const int h = it.kv_head * G + (r - j * G);
         row_pos[rt] = valid ? pr.pos0 + j : 0x3fffffff;
-        const uint4 *qrow = reinterpret_cast<const uint4 *>(pr.Q) + (size_t)(valid ? h * pr.rows + j : 0) * NCH;
+        const gptr<const u32x4> qrow = as_global(reinterpret_cast<const u32x4 *>(pr.Q)) + (size_t)(valid ? h * pr.rows + j : 0) * NCH;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[rt][ks] = __builtin_bit_cast(bf16x8, valid ? qrow[4 * ks + lg] : make_uint4(0, 0, 0, 0));
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 q = valid ? qrow[4 * ks + lg] : u32x4{0u, 0u, 0u, 0u};
+            qf[rt][ks] = __builtin_bit_cast(bf16x8, q);
+        }
     }
 
     // Per-lane LDS byte offsets inside a tile.
@@ -225,17 +228,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
         }
     };
 
-    // Descriptors run two tiles ahead of use and data one tile ahead, so a
-    // tile's loads never wait on a descriptor fetched in the same iteration.
-    auto desc = [&](int tt) { return fetch_tile(pr.tiles, min(tt, n_kt - 1)); };
+    // Descriptors are loaded two tiles ahead of use and data one tile ahead;
+    // a descriptor reaches scalar registers one iteration after its load.
+    auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
     if (n_kt > 0) {
-        TileSR cur = desc(0), nxt = desc(1);
+        TileSR cur = to_sr(desc(0));
+        uint32_t nraw = desc(1);
         stage_store<NCH, SLD, false>(stage_load<NCH, SLD, false>(cur, it.kv_head, tid), lds_k[0], lds_v[0], tid);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
             const bool more = tt + 1 < n_kt;
-            const TileSR nn = desc(tt + 2);
+            const TileSR nxt = to_sr(nraw);
+            nraw = desc(tt + 2);
             Staged<SLD> st;
             if (more)
                 st = stage_load<NCH, SLD, false>(nxt, it.kv_head, tid);
@@ -248,7 +253,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
                 stage_store<NCH, SLD, false>(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
             __syncthreads();
             cur = nxt;
-            nxt = nn;
         }
     }
 
@@ -271,7 +275,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
         for (int dt = 0; dt < DT; ++dt)
             o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float *partial = pr.partial + (size_t)it.slot * pr.n_keys;
+    const gptr<float> partial = as_global(pr.partial) + (size_t)it.slot * pr.n_keys;
     auto flush_impact = [&](int tt, TileSR kt, int buf) {
         if (wave == (tt & 3)) {
             if (lane < kt.n_valid)
@@ -354,13 +358,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
     };
 
     if (n_kt > 0) {
-        TileSR cur = desc(0), nxt = desc(1), prev = cur;
+        TileSR cur = to_sr(desc(0)), prev = cur;
+        uint32_t nraw = desc(1);
         stage_store<NCH, SLD, true>(stage_load<NCH, SLD, true>(cur, it.kv_head, tid), lds_k[0], lds_v[0], tid);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
             const bool more = tt + 1 < n_kt;
-            const TileSR nn = desc(tt + 2);
+            const TileSR nxt = to_sr(nraw);
+            nraw = desc(tt + 2);
             Staged<SLD> st;
             if (more)
                 st = stage_load<NCH, SLD, true>(nxt, it.kv_head, tid);
@@ -376,7 +382,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
             __syncthreads();
             prev = cur;
             cur = nxt;
-            nxt = nn;
         }
         flush_impact(n_kt - 1, prev, (n_kt - 1) & 1);
     }
@@ -389,7 +394,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
             continue;
         const int j = r / G;
         const int h = it.kv_head * G + (r - j * G);
-        uint16_t *orow = reinterpret_cast<uint16_t *>(pr.out) + ((size_t)h * pr.rows + j) * D;
+        const gptr<uint16_t> orow = as_global(reinterpret_cast<uint16_t *>(pr.out)) + ((size_t)h * pr.rows + j) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const __bf16 b0 = (__bf16)o[rt][dt][0], b1 = (__bf16)o[rt][dt][1];
@@ -398,7 +403,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
                                 ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
             const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-            *reinterpret_cast<uint2 *>(orow + 16 * dt + 4 * lg) = make_uint2(lo, hi);
+            *reinterpret_cast<gptr<u32x2>>(orow + 16 * dt + 4 * lg) = u32x2{lo, hi};
         }
     }
 }

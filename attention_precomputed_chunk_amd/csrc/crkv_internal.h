@@ -38,6 +38,7 @@ struct KTile {
     int32_t seg_len;    // keys in the segment (the KV-head stride in rows)
     int32_t seg_lo;     // global position of the segment's first key
 };
+static_assert(sizeof(KTile) == 32, "kernels read a KTile as eight dwords");
 
 struct ProbDesc {
     const void *Q;          // [H][rows][d]

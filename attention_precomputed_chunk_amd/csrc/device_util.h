@@ -10,6 +10,21 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef short i16x4 __attribute__((__vector_size__(8)));
 typedef short i16x8 __attribute__((__vector_size__(16)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Pointers into the global address space: loads and stores through them are
+// global_* instructions, which count only against vmcnt. Generic (flat)
+// accesses also count against lgkmcnt, so every wait for an LDS read would
+// wait for outstanding HBM loads as well.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+
+template <typename T>
+__device__ __forceinline__ gptr<T> as_global(T *p)
+{
+    return (gptr<T>)p;
+}
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
