@@ -10,7 +10,8 @@ Functions carry the C names:
 * ``crkv_attn_chunks(Q, chunk_K, chunk_V, chunk_len, m, q_len, H, H_kv, d, out, impact, ...)``
 * ``crkv_attn_chunks_batched(problems, H, H_kv, d, ...)``
 * ``crkv_topk(impact, n, k, idx, ...)`` and ``crkv_topk_batched(...)``
-* ``crkv_budget(n_doc, r)``, ``crkv_workspace_size(...)``, ``crkv_version()``
+* ``crkv_budget(n_doc, r)``, ``crkv_workspace_size(...)``, ``crkv_plan_info(...)``,
+  ``crkv_version()``
 """
 from __future__ import annotations
 
@@ -54,8 +55,8 @@ class crkv_problem(ctypes.Structure):
 _lib = None
 
 DECLARED = ["crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
-            "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_status_string",
-            "crkv_last_error", "crkv_version"]
+            "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
+            "crkv_status_string", "crkv_last_error", "crkv_version"]
 
 
 def lib():
@@ -90,6 +91,10 @@ def lib():
         L.crkv_workspace_size.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
                                           ctypes.POINTER(crkv_opts)]
         L.crkv_workspace_size.restype = ctypes.c_size_t
+        L.crkv_plan_info.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                     ctypes.POINTER(crkv_opts), ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                     ctypes.POINTER(c_int)]
+        L.crkv_plan_info.restype = c_int
         L.crkv_status_string.argtypes = [c_int]
         L.crkv_status_string.restype = ctypes.c_char_p
         L.crkv_last_error.argtypes = []
@@ -191,6 +196,20 @@ def crkv_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int, mod
     keep, arr = _problems(problems)
     o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream=0)
     return int(lib().crkv_workspace_size(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+PLAN_KERNELS = {0: "f32", 1: "bf16_wave", 2: "bf16_pair"}
+
+
+def crkv_plan_info(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: str = "query",
+                   dtype: Optional[int] = None) -> dict:
+    """Launch configuration the planner picks: kernel name, row tiles, workgroups."""
+    keep, arr = _problems(problems)
+    o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream=0)
+    k, rt, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().crkv_plan_info(arr, len(keep), H, H_kv, d, ctypes.byref(o), ctypes.byref(k),
+                                ctypes.byref(rt), ctypes.byref(wg)))
+    return {"kernel": PLAN_KERNELS[k.value], "row_tiles": rt.value, "workgroups": wg.value}
 
 
 def crkv_topk(impact, n: int, k: int, idx, stream=None):

@@ -1,0 +1,208 @@
+// Helpers shared by the gfx950 bf16 attention kernels: LDS tile layout, key
+// tile descriptors, global-to-LDS staging and the score MFMAs.
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16, 64 lanes; li = lane % 16,
+// lg = lane / 16). Scores are taken as S^T = K . Q^T: A = 16 keys x 32 d from
+// LDS, B = 32 d x 16 rows held in registers for the whole sweep. The
+// accumulator gives lane (li, lg) row li and four keys. The A rows of the two
+// 16-key subtiles of a 32-key tile are permuted so that lane (li, lg) ends up
+// holding keys 8lg .. 8lg+7, which rounded to bf16 are exactly the B operand of
+// O^T = V^T . P^T. The V^T operand comes from V stored row-major in LDS
+// through ds_read_b64_tr_b16: inside each 16-lane group, if lane j reads four
+// bf16 B[j][0..3], lane i receives B[4e + i/4][i % 4] (e = 0..3), so lane j
+// addresses V[key0 + j/4][d0 + 4(j%4)] and two such reads give lane i the
+// eight keys of column d0 + i.
+#pragma once
+#include "device_util.h"
+
+namespace crkv {
+
+constexpr int kWsThreads = 2 * kWaves * 64;   // pair kernel: a producer and a consumer wave per SIMD
+
+// K tile slot of 16-byte chunk `ch` of row `key`: the 16 keys one A operand
+// reads (keys 8(i>>2) + 4s + (i&3)) land in 16 distinct slots.
+template <int NCH>
+__device__ __forceinline__ int kswz(int key)
+{
+    return NCH == 16 ? ((key & 3) | (((key >> 3) & 3) << 2)) : ((key & 3) | (((key >> 3) & 1) << 2));
+}
+// V tile: even XOR values keep each 32-byte pair of chunks together, and the
+// rows one transposed read touches (4 consecutive keys, 8 for two lane
+// groups) get distinct 32-byte bank groups.
+template <int NCH>
+__device__ __forceinline__ int vswz(int key)
+{
+    return NCH == 16 ? 2 * ((key & 3) | (((key >> 3) & 1) << 2)) : 2 * (key & 3);
+}
+
+// A key tile's descriptor held in scalar registers (passed by value so it is
+// never demoted to scratch memory).
+struct TileSR {
+    gptr<const u32x4> K;
+    gptr<const u32x4> V;
+    int n_valid, key0, seg_len, seg_lo;
+};
+
+// A descriptor is eight dwords; lane l loads dword l % 8 with a vector load,
+// one iteration before the dwords are moved to scalar registers, so the
+// load's latency is covered by a tile of work. (A scalar load would count
+// against lgkmcnt and be waited for with the next LDS read.)
+__device__ __forceinline__ uint32_t load_tile(const KTile *tiles, int i, int lane)
+{
+    return as_global(reinterpret_cast<const uint32_t *>(tiles))[(size_t)i * 8 + (lane & 7)];
+}
+
+__device__ __forceinline__ TileSR to_sr(uint32_t raw)
+{
+    auto dw = [&](int j) { return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)raw, j); };
+    TileSR r;
+    r.K = reinterpret_cast<gptr<const u32x4>>(dw(0) | (dw(1) << 32));
+    r.V = reinterpret_cast<gptr<const u32x4>>(dw(2) | (dw(3) << 32));
+    r.n_valid = (int)dw(4);
+    r.key0 = (int)dw(5);
+    r.seg_len = (int)dw(6);
+    r.seg_lo = (int)dw(7);
+    return r;
+}
+
+// One key tile's K (and V) 16-byte chunks in flight from global memory to LDS,
+// spread over NT threads: thread t moves chunks t + i NT (i < PER). Chunk index
+// x < CH is K chunk x, else V chunk x - CH; chunk c of a tile is key c / NCH,
+// column chunk c % NCH. Returned and passed by value so that it stays in
+// registers.
+template <int NCH, bool WITH_V, int NT>
+struct Staged {
+    static constexpr int CH = kKeyTile * NCH;
+    static constexpr int TOTAL = WITH_V ? 2 * CH : CH;
+    static constexpr int PER = (TOTAL + NT - 1) / NT;
+    static_assert(!WITH_V || CH % NT == 0, "K and V chunks split evenly over the threads");
+    u32x4 c[PER];
+};
+
+// A thread's fixed part of the staging: which chunk it moves and where the
+// chunk lands in a tile buffer (the swizzled LDS byte offset), computed once.
+template <int NCH, bool WITH_V, int NT>
+struct Stager {
+    using S = Staged<NCH, WITH_V, NT>;
+    static constexpr int ROW = NCH * 16;
+    static constexpr bool is_v(int i) { return WITH_V && i * NT >= S::CH; }
+    int chunk[S::PER];      // chunk index inside its K (or V) tile, -1 if none
+    uint32_t lds[S::PER];   // LDS byte offset inside a tile buffer
+
+    __device__ __forceinline__ explicit Stager(int t)
+    {
+#pragma unroll
+        for (int i = 0; i < S::PER; ++i) {
+            const int x = t + i * NT;
+            const int c = is_v(i) ? x - S::CH : x;
+            const int key = c / NCH, ch = c % NCH;
+            const int sw = is_v(i) ? vswz<NCH>(key) : kswz<NCH>(key);
+            chunk[i] = x < S::TOTAL ? c : -1;
+            lds[i] = (uint32_t)(key * ROW + ((ch ^ sw) << 4));
+        }
+    }
+
+    // Row `key` of KV head g of the tile's segment starts g * seg_len rows past
+    // the tile's base; keys past n_valid repeat the last real key (masked later).
+    __device__ __forceinline__ S load(TileSR kt, int kv_head) const
+    {
+        S st;
+        const size_t head = (size_t)kv_head * kt.seg_len * NCH;
+        const gptr<const u32x4> kb = kt.K + head, vb = kt.V + head;
+        if (kt.n_valid == kKeyTile) {
+#pragma unroll
+            for (int i = 0; i < S::PER; ++i)
+                if (chunk[i] >= 0)
+                    st.c[i] = is_v(i) ? vb[chunk[i]] : kb[chunk[i]];
+        } else {
+#pragma unroll
+            for (int i = 0; i < S::PER; ++i)
+                if (chunk[i] >= 0) {
+                    const int c = min(chunk[i] / NCH, kt.n_valid - 1) * NCH + chunk[i] % NCH;
+                    st.c[i] = is_v(i) ? vb[c] : kb[c];
+                }
+        }
+        return st;
+    }
+
+    __device__ __forceinline__ void store(const S st, unsigned char *lk, unsigned char *lv) const
+    {
+#pragma unroll
+        for (int i = 0; i < S::PER; ++i)
+            if (chunk[i] >= 0)
+                *reinterpret_cast<u32x4 *>((is_v(i) ? lv : lk) + lds[i]) = st.c[i];
+    }
+};
+
+// Tiles t + 1 .. t + DEPTH in flight from global memory while tile t is in
+// use: a tile's loads are issued DEPTH steps before its LDS store, so the
+// memory latency is covered by DEPTH steps of work rather than one. Slots
+// shift down by one per step (static indices keep them in registers).
+template <int NCH, bool WITH_V, int NT, int DEPTH>
+struct Ring {
+    Staged<NCH, WITH_V, NT> s[DEPTH];
+};
+
+template <int NCH, bool WITH_V, int NT, int DEPTH>
+__device__ __forceinline__ void ring_shift(Ring<NCH, WITH_V, NT, DEPTH> &r)
+{
+#pragma unroll
+    for (int i = 0; i + 1 < DEPTH; ++i)
+        r.s[i] = r.s[i + 1];
+}
+
+// S^T of one 16-row tile against the two 16-key subtiles of a key tile.
+struct Spair {
+    f32x4 s0, s1;
+};
+
+template <int KS>
+__device__ __forceinline__ Spair scores(const bf16x8 (&kf)[2][KS], const bf16x8 (&q)[KS])
+{
+    Spair r;
+    r.s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    r.s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        r.s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], q[ks], r.s0, 0, 0, 0);
+        r.s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], q[ks], r.s1, 0, 0, 0);
+    }
+    return r;
+}
+
+// Scores past the tile's valid keys or past the row's causal limit (`lim`,
+// relative to the tile's first key) become -inf.
+__device__ __forceinline__ void mask_scores(Spair &s, int lim, int lg)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (8 * lg + e > lim)
+            s.s0[e] = -INFINITY;
+        if (8 * lg + 4 + e > lim)
+            s.s1[e] = -INFINITY;
+    }
+}
+
+// Q^T fragments of row tile t: packed row r = 16 t + li is query row r / G of
+// head kv_head * G + r % G; rows past the packed total are padding (zero Q,
+// position beyond every key).
+template <int KS>
+__device__ __forceinline__ void load_q_rows(const ProbDesc &pr, const ItemDesc &it, int G, int t, int li,
+                                            int lg, bf16x8 (&q)[KS], int &row_pos)
+{
+    constexpr int NCH = KS * 4;
+    const int r = t * kRowTile + li;
+    const bool valid = r < G * pr.rows;
+    const int j = r / G;
+    const int h = it.kv_head * G + (r - j * G);
+    row_pos = valid ? pr.pos0 + j : 0x3fffffff;
+    const gptr<const u32x4> qrow =
+        as_global(reinterpret_cast<const u32x4 *>(pr.Q)) + (size_t)(valid ? h * pr.rows + j : 0) * NCH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 v = valid ? qrow[4 * ks + lg] : u32x4{0u, 0u, 0u, 0u};
+        q[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+}  // namespace crkv

@@ -1,0 +1,377 @@
+// bf16 attention of query rows over a segment table of precomputed K/V
+// chunks, with per-key impact partials, for gfx950 (CDNA4): the
+// producer/consumer wave-pair kernel.
+//
+// What is computed (TurboRAG summary: K_combined = Concat(K^(1..m), K^(Q)) and
+// the causal attention equation; CacheBlend summary: the Impact equation and
+// the selective-recompute listing's softmax and column sum):
+//   s_ji  = q_j . k_i / sqrt(d)      for keys at positions <= the row's
+//   p_ji  = exp(s_ji - lse_j),  lse_j = log sum_i exp(s_ji)
+//   out_j = sum_i p_ji v_i
+//   imp_i = sum over heads and counted rows of p_ji
+//
+// Exact impact needs every row's final lse before any column sum, so each
+// workgroup sweeps its keys twice: sweep 1 computes the row lse, sweep 2
+// recomputes the scores, forms p in fp32, accumulates the impact column sums
+// from the fp32 p, and runs P.V on the matrix cores with p rounded to bf16.
+//
+// The MFMA operand layout is described in attn_bf16_common.h.
+//
+// Waves and SIMDs. A wave issues in order and at most one instruction every
+// few cycles, so a lone wave per SIMD leaves the matrix core idle while it
+// works through the softmax and cannot hide the latency of its own
+// dependences. Two waves per SIMD overlap one's vector work with the other's
+// matrix work, but cannot each hold Q, K and V fragments and a d = 128 output
+// accumulator in 256 registers. The workgroup therefore has 8 waves (waves w
+// and w + 4 share a SIMD) with roles:
+//   * sweep 1: every wave takes RT/2 row tiles and computes their lse;
+//   * sweep 2: wave p < 4 (producer) holds Q of RT row tiles, computes S and
+//     p and the impact column sums, and writes P^T fragments (bf16) to LDS;
+//     wave p + 4 (consumer) holds the O accumulators of the same rows and
+//     runs P.V on the key tile the producer finished one step earlier.
+// Each role runs its own loop, so the register allocator never holds Q and O
+// at once; both loops meet the same barriers (one per step). LDS holds K
+// twice (tile being scored, tile being staged), V three times (tile in P.V,
+// tile being scored, tile being staged) and P^T twice.
+//
+// Work decomposition: one workgroup per (problem, KV head, block of 4 * RT row
+// tiles). The rows of the G query heads sharing a KV head are packed as
+// (query row j, head h) so one K/V tile in LDS serves the group.
+#include <type_traits>
+
+#include "attn_bf16_common.h"
+
+namespace crkv {
+
+constexpr int kDepth1 = 2;                     // tiles in flight, sweep 1 (K only)
+constexpr int kDepth2 = 1;                     // tiles in flight, sweep 2 (K and V)
+
+template <int D, int RT, bool CROSS>
+__global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnArgs a)
+{
+    constexpr int RT1 = RT / 2;                // row tiles per wave in sweep 1
+    constexpr int KS = D / 32;                 // MFMA k-steps along d
+    constexpr int DT = D / 16;                 // output d tiles
+    constexpr int NCH = D / 8;                 // 16-byte chunks per row
+    constexpr int ROW = 2 * D;                 // LDS bytes per K or V row
+    constexpr int TILE = kKeyTile * ROW;       // LDS bytes per K (or V) tile
+    static_assert(kKeyTile == 32 && RT % 2 == 0, "tile geometry");
+
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_v[3][TILE];
+    __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][kWaves][RT][64];
+    __shared__ __attribute__((aligned(16))) float lds_imp[2][kWaves][kKeyTile];
+    __shared__ float lds_lse[kWaves * RT * kRowTile];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    const ItemDesc it = a.items[blockIdx.x];
+    if (it.n_rowtiles == 0)
+        return;
+    const ProbDesc pr = a.probs[it.prob];
+    const int G = a.G;
+    const float c = a.c_log2;
+    const int n_kt = it.n_ktiles;
+    if (n_kt == 0)
+        return;
+
+    // Per-lane LDS byte offsets inside a tile.
+    const int kkey0 = 8 * (li >> 2) + (li & 3);          // A row li of subtile 0 (subtile 1: +4)
+    const int ksw = kswz<NCH>(kkey0);                     // same for kkey0 + 4
+    auto k_off = [&](int sub, int ks) { return (kkey0 + 4 * sub) * ROW + (((4 * ks + lg) ^ ksw) << 4); };
+    auto v_off = [&](int dt, int r) {
+        const int key = 8 * lg + 4 * r + (li >> 2);
+        const int d = 16 * dt + 4 * (li & 3);
+        return key * ROW + (((d >> 3) ^ vswz<NCH>(key)) << 4) + (d & 7) * 2;
+    };
+    auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
+    auto min_pos = [&](int t0) { return pr.pos0 + (t0 * kRowTile) / G; };
+
+    // ---------------------------------------------------------------- sweep 1: row lse (all waves)
+    {
+        const int t0 = it.tile_begin + wave * RT1;
+        const int wave_min_pos = min_pos(t0);
+        bf16x8 qf[RT1][KS];
+        int row_pos[RT1];
+        float row_m[RT1], row_l[RT1];
+#pragma unroll
+        for (int rt = 0; rt < RT1; ++rt) {
+            load_q_rows<KS>(pr, it, G, t0 + rt, li, lg, qf[rt], row_pos[rt]);
+            row_m[rt] = -INFINITY;
+            row_l[rt] = 0.f;
+        }
+        auto tile = [&](TileSR kt, int buf, auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            bf16x8 kf[2][KS];
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+#pragma unroll
+            for (int rt = 0; rt < RT1; ++rt) {
+                Spair sc = scores<KS>(kf, qf[rt]);
+                if constexpr (MASK)
+                    mask_scores(sc, min(kt.n_valid - 1, row_pos[rt] - kt.key0), lg);
+                const f32x4 s0 = sc.s0, s1 = sc.s1;
+                const float tmax = fmaxf(fmaxf(fmaxf(row_m[rt], s0[0]), fmaxf(s0[1], s0[2])),
+                                         fmaxf(fmaxf(s0[3], s1[0]), fmaxf(fmaxf(s1[1], s1[2]), s1[3])));
+                const float mc = ((tmax == -INFINITY) ? 0.f : tmax) * c;
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sum += exp2_hw(__builtin_fmaf(s0[e], c, -mc)) + exp2_hw(__builtin_fmaf(s1[e], c, -mc));
+                row_l[rt] = __builtin_fmaf(row_l[rt], exp2_hw(__builtin_fmaf(row_m[rt], c, -mc)), sum);
+                row_m[rt] = tmax;
+            }
+        };
+        using R1 = Ring<NCH, false, kWsThreads, kDepth1>;
+        const Stager<NCH, false, kWsThreads> stg(tid);
+        R1 ring;
+        stg.store(stg.load(to_sr(desc(0)), it.kv_head), lds_k[0], lds_v[0]);
+#pragma unroll
+        for (int i = 1; i < kDepth1; ++i)
+            if (i < n_kt)
+                ring.s[i - 1] = stg.load(to_sr(desc(i)), it.kv_head);
+        TileSR cur = to_sr(desc(0));
+        uint32_t craw = desc(1), sraw = desc(kDepth1);
+        __syncthreads();
+        for (int tt = 0; tt < n_kt; ++tt) {
+            const int buf = tt & 1;
+            const TileSR nxt = to_sr(craw);
+            craw = desc(tt + 2);
+            const TileSR stile = to_sr(sraw);
+            sraw = desc(tt + kDepth1 + 1);
+            if (tt + kDepth1 < n_kt)
+                ring.s[kDepth1 - 1] = stg.load(stile, it.kv_head);
+            if ((cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos))
+                tile(cur, buf, std::true_type{});
+            else
+                tile(cur, buf, std::false_type{});
+            if (tt + 1 < n_kt)
+                stg.store(ring.s[0], lds_k[buf ^ 1], lds_v[0]);
+            ring_shift(ring);
+            __syncthreads();
+            cur = nxt;
+        }
+        // Combine the four lane groups of each row into its log2-domain lse;
+        // padded rows get +inf so every weight they would produce is 0.
+#pragma unroll
+        for (int rt = 0; rt < RT1; ++rt) {
+            float m = row_m[rt], l = row_l[rt];
+            merge_state(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16), c);
+            merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32), c);
+            if (lg == 0)
+                lds_lse[(wave * RT1 + rt) * kRowTile + li] =
+                    (row_pos[rt] < 0x3fffffff) ? m * c + __log2f(l) : INFINITY;
+        }
+    }
+
+    // ---------------------------------------------------------------- sweep 2
+    // Step s (0 <= s <= n_kt): the producers score key tile s from lds_k[s & 1]
+    // and write its P^T to lds_p[s & 1]; the consumers run P.V of tile s - 1
+    // from lds_p[(s - 1) & 1] and lds_v[(s - 1) % 3] and flush its impact;
+    // the producers store tile s + 1 into lds_k[(s + 1) & 1], lds_v[(s + 1) % 3]
+    // (loaded kDepth2 steps earlier) and start the loads of tile s + kDepth2.
+    // Every read of a buffer ends before the barrier after which it is refilled.
+    constexpr int NTP = kWaves * 64;   // the producers stage the tiles of sweep 2
+    using R2 = Ring<NCH, true, NTP, kDepth2>;
+    R2 ring2;
+    const Stager<NCH, true, NTP> stg2(tid & (NTP - 1));
+    if (wave < kWaves) {
+        stg2.store(stg2.load(to_sr(desc(0)), it.kv_head), lds_k[0], lds_v[0]);
+#pragma unroll
+        for (int i = 1; i < kDepth2; ++i)
+            if (i < n_kt)
+                ring2.s[i - 1] = stg2.load(to_sr(desc(i)), it.kv_head);
+    }
+    __syncthreads();   // also publishes lds_lse
+
+    const int pair = wave & (kWaves - 1);
+    const int t0 = it.tile_begin + pair * RT;
+    if (wave < kWaves) {
+        // ------------------------------------------------------------ producer
+        const int wave_min_pos = min_pos(t0);
+        bf16x8 qf[RT][KS];
+        int row_pos[RT];
+        float lse2[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            load_q_rows<KS>(pr, it, G, t0 + rt, li, lg, qf[rt], row_pos[rt]);
+            lse2[rt] = lds_lse[(pair * RT + rt) * kRowTile + li];
+        }
+        auto tile = [&](TileSR kt, int buf, auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            bf16x8 kf[2][KS];
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+            float imp[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                imp[i] = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                Spair sc = scores<KS>(kf, qf[rt]);
+                if constexpr (MASK)
+                    mask_scores(sc, min(kt.n_valid - 1, row_pos[rt] - kt.key0), lg);
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[e] = exp2_hw(__builtin_fmaf(sc.s0[e], c, -lse2[rt]));
+                    p[4 + e] = exp2_hw(__builtin_fmaf(sc.s1[e], c, -lse2[rt]));
+                }
+                if constexpr (CROSS) {
+                    // rows inside the tile's own segment do not count
+                    const float w =
+                        (row_pos[rt] >= kt.seg_lo && row_pos[rt] < kt.seg_lo + kt.seg_len) ? 0.f : 1.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        imp[i] = __builtin_fmaf(p[i], w, imp[i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        imp[i] += p[i];
+                }
+                bf16x8 pb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    pb[i] = (__bf16)p[i];
+                lds_p[buf][pair][rt][lane] = pb;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                imp[i] = row16_sum(imp[i]);
+            if (li == 0) {
+                float *dst = &lds_imp[buf][pair][8 * lg];
+                *reinterpret_cast<float4 *>(dst) = make_float4(imp[0], imp[1], imp[2], imp[3]);
+                *reinterpret_cast<float4 *>(dst + 4) = make_float4(imp[4], imp[5], imp[6], imp[7]);
+            }
+        };
+        TileSR cur = to_sr(desc(0));
+        uint32_t craw = desc(1), sraw = desc(kDepth2);
+        int vb = 1;   // lds_v slot of tile s + 1
+        for (int s = 0; s <= n_kt; ++s) {
+            const TileSR nxt = to_sr(craw);
+            craw = desc(s + 2);
+            const TileSR stile = to_sr(sraw);
+            sraw = desc(s + kDepth2 + 1);
+            if (s + kDepth2 < n_kt)
+                ring2.s[kDepth2 - 1] = stg2.load(stile, it.kv_head);
+            if (s < n_kt) {
+                if ((cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos))
+                    tile(cur, s & 1, std::true_type{});
+                else
+                    tile(cur, s & 1, std::false_type{});
+            }
+            if (s + 1 < n_kt)
+                stg2.store(ring2.s[0], lds_k[(s + 1) & 1], lds_v[vb]);
+            ring_shift(ring2);
+            __syncthreads();
+            cur = nxt;
+            vb = vb == 2 ? 0 : vb + 1;
+        }
+    } else {
+        // ------------------------------------------------------------ consumer
+        f32x4 o[RT][DT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const gptr<float> partial = as_global(pr.partial) + (size_t)it.slot * pr.n_keys;
+        TileSR cur = to_sr(desc(0)), prev = cur;
+        uint32_t nraw = desc(1);
+        int vb = 1;   // lds_v slot of tile s + 1; tile s - 1 sits in the next slot (mod 3)
+        for (int s = 0; s <= n_kt; ++s) {
+            const TileSR nxt = to_sr(nraw);
+            nraw = desc(s + 2);
+            if (s > 0) {
+                const int pbuf = (s - 1) & 1;
+                const int vprev = vb == 2 ? 0 : vb + 1;
+                // impact of tile s - 1: one consumer adds the four producers' column sums
+                if (pair == ((s - 1) & (kWaves - 1)) && lane < prev.n_valid)
+                    partial[prev.key0 + lane] = lds_imp[pbuf][0][lane] + lds_imp[pbuf][1][lane] +
+                                                lds_imp[pbuf][2][lane] + lds_imp[pbuf][3][lane];
+                bf16x8 pb[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    pb[rt] = lds_p[pbuf][pair][rt][lane];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(&lds_v[vprev][v_off(dt, 0)]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(&lds_v[vprev][v_off(dt, 1)]));
+                    const bf16x8 vf =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[rt][dt], 0, 0, 0);
+                }
+            }
+            __syncthreads();
+            prev = cur;
+            cur = nxt;
+            vb = vb == 2 ? 0 : vb + 1;
+        }
+
+        // ------------------------------------------------------------ epilogue: out rows
+        const int packed_total = G * pr.rows;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = (t0 + rt) * kRowTile + li;
+            if (r >= packed_total)
+                continue;
+            const int j = r / G;
+            const int h = it.kv_head * G + (r - j * G);
+            const gptr<uint16_t> orow =
+                as_global(reinterpret_cast<uint16_t *>(pr.out)) + ((size_t)h * pr.rows + j) * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const __bf16 b0 = (__bf16)o[rt][dt][0], b1 = (__bf16)o[rt][dt][1];
+                const __bf16 b2 = (__bf16)o[rt][dt][2], b3 = (__bf16)o[rt][dt][3];
+                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+                *reinterpret_cast<gptr<u32x2>>(orow + 16 * dt + 4 * lg) = u32x2{lo, hi};
+            }
+        }
+    }
+}
+
+template <int D, int RT>
+static void launch_pair_rt(const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    if (args.cross)
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, RT, true>), dim3(n_items), dim3(kWsThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, RT, false>), dim3(n_items), dim3(kWsThreads), 0, stream, args);
+}
+
+template <int D>
+static hipError_t launch_pair_d(int rt, const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    switch (rt) {
+    case 2: launch_pair_rt<D, 2>(args, n_items, stream); break;
+    case 4: launch_pair_rt<D, 4>(args, n_items, stream); break;
+    case 6: launch_pair_rt<D, 6>(args, n_items, stream); break;
+    default: return hipErrorInvalidValue;   // no such build; the planner never asks for it
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_pair(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    if (n_items <= 0)
+        return hipSuccess;
+    return d == 128 ? launch_pair_d<128>(rt, args, n_items, stream) : launch_pair_d<64>(rt, args, n_items, stream);
+}
+
+}  // namespace crkv

@@ -1,5 +1,6 @@
 // bf16 attention of query rows over a segment table of precomputed K/V
-// chunks, with per-key impact partials, for gfx950 (CDNA4).
+// chunks, with per-key impact partials, for gfx950 (CDNA4): the one-wave-per-
+// SIMD kernel.
 //
 // What is computed (TurboRAG summary: K_combined = Concat(K^(1..m), K^(Q)) and
 // the causal attention equation; CacheBlend summary: the Impact equation and
@@ -14,129 +15,37 @@
 // recomputes the scores, forms p in fp32, accumulates the impact column sums
 // from the fp32 p, and runs P.V on the matrix cores with p rounded to bf16.
 //
-// Matrix-core layout (v_mfma_f32_16x16x32_bf16, 64 lanes; li = lane % 16,
-// lg = lane / 16). Scores are taken as S^T = K . Q^T: A = 16 keys x 32 d from
-// LDS, B = 32 d x 16 rows held in registers for the whole sweep. The
-// accumulator gives lane (li, lg) row li and four keys. The A rows of the two
-// 16-key subtiles of a 32-key tile are permuted so that lane (li, lg) ends up
-// holding keys 8lg .. 8lg+7, which rounded to bf16 are exactly the B operand of
-// O^T = V^T . P^T, so P never leaves registers. The V^T operand comes from V
-// stored row-major in LDS through ds_read_b64_tr_b16: inside each 16-lane
-// group, if lane j reads four bf16 B[j][0..3], lane i receives
-// B[4e + i/4][i % 4] (e = 0..3), so lane j addresses V[key0 + j/4][d0 + 4(j%4)]
-// and two such reads give lane i the eight keys of column d0 + i.
+// The MFMA operand layout is described in attn_bf16_common.h.
 //
-// On gfx950 the matrix cores and the vector ALU of a SIMD hardly overlap, so
-// the kernel keeps both instruction streams short: no per-row-tile branches
-// (each wave owns a compile-time number of 16-row tiles, padded rows are
-// masked by an infinite lse), K/V tiles staged through 16 registers per
-// thread, one barrier per 32-key tile.
+// One wave per SIMD holds every role: Q fragments, the scores, the softmax and
+// the O accumulators of its row tiles, so a KV head's rows fit in fewer
+// workgroups than with the producer/consumer pairs of attn_bf16_pair.hip (up
+// to 4 * 7 row tiles against 4 * 6), at the price of a wave that cannot hide
+// its own dependence latencies. Each wave owns a compile-time number of
+// 16-row tiles (no per-row-tile branches; padded rows are masked by an
+// infinite lse), K/V tiles are staged through registers, and there is one
+// barrier per 32-key tile.
 //
 // Work decomposition: one workgroup of 4 waves per (problem, KV head, block of
 // 4 * RT row tiles). The rows of the G query heads sharing a KV head are
 // packed as (query row j, head h) so one K/V tile in LDS serves the group.
 #include <type_traits>
 
-#include "device_util.h"
+#include "attn_bf16_common.h"
 
 namespace crkv {
 
-// K tile slot of 16-byte chunk `ch` of row `key`: the 16 keys one A operand
-// reads (keys 8(i>>2) + 4s + (i&3)) land in 16 distinct slots.
-template <int NCH>
-__device__ __forceinline__ int kswz(int key)
-{
-    return NCH == 16 ? ((key & 3) | (((key >> 3) & 3) << 2)) : ((key & 3) | (((key >> 3) & 1) << 2));
-}
-// V tile: even XOR values keep each 32-byte pair of chunks together, and the
-// rows one transposed read touches (4 consecutive keys, 8 for two lane
-// groups) get distinct 32-byte bank groups.
-template <int NCH>
-__device__ __forceinline__ int vswz(int key)
-{
-    return NCH == 16 ? 2 * ((key & 3) | (((key >> 3) & 1) << 2)) : 2 * (key & 3);
-}
-
-// A key tile's descriptor held in scalar registers (passed by value so it is
-// never demoted to scratch memory).
-struct TileSR {
-    gptr<const u32x4> K;
-    gptr<const u32x4> V;
-    int n_valid, key0, seg_len, seg_lo;
-};
-
-// A descriptor is eight dwords; lane l loads dword l % 8 with a vector load,
-// one iteration before the dwords are moved to scalar registers, so the
-// load's latency is covered by a tile of work. (A scalar load would count
-// against lgkmcnt and be waited for with the next LDS read.)
-__device__ __forceinline__ uint32_t load_tile(const KTile *tiles, int i, int lane)
-{
-    return as_global(reinterpret_cast<const uint32_t *>(tiles))[(size_t)i * 8 + (lane & 7)];
-}
-
-__device__ __forceinline__ TileSR to_sr(uint32_t raw)
-{
-    auto dw = [&](int j) { return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)raw, j); };
-    TileSR r;
-    r.K = reinterpret_cast<gptr<const u32x4>>(dw(0) | (dw(1) << 32));
-    r.V = reinterpret_cast<gptr<const u32x4>>(dw(2) | (dw(3) << 32));
-    r.n_valid = (int)dw(4);
-    r.key0 = (int)dw(5);
-    r.seg_len = (int)dw(6);
-    r.seg_lo = (int)dw(7);
-    return r;
-}
-
-// One tile's K (and V) chunks in flight from global memory to LDS. Returned
-// and passed by value so that it stays in registers.
-template <int SLD>
-struct Staged {
-    u32x4 k[SLD];
-    u32x4 v[SLD];
-};
-
-template <int NCH, int SLD, bool WITH_V>
-__device__ __forceinline__ Staged<SLD> stage_load(TileSR kt, int kv_head, int tid)
-{
-    Staged<SLD> st;
-    const size_t base = (size_t)kv_head * kt.seg_len * NCH;
-#pragma unroll
-    for (int i = 0; i < SLD; ++i) {
-        const int cidx = tid + i * kThreads;
-        const int key = min(cidx / NCH, kt.n_valid - 1);   // missing keys repeat a real one; masked later
-        const int ch = cidx % NCH;
-        st.k[i] = kt.K[base + (size_t)key * NCH + ch];
-        if constexpr (WITH_V)
-            st.v[i] = kt.V[base + (size_t)key * NCH + ch];
-    }
-    return st;
-}
-
-template <int NCH, int SLD, bool WITH_V>
-__device__ __forceinline__ void stage_store(const Staged<SLD> st, unsigned char *lk, unsigned char *lv,
-                                            int tid)
-{
-    constexpr int ROW = NCH * 16;
-#pragma unroll
-    for (int i = 0; i < SLD; ++i) {
-        const int cidx = tid + i * kThreads;
-        const int key = cidx / NCH, ch = cidx % NCH;
-        *reinterpret_cast<u32x4 *>(lk + key * ROW + ((ch ^ kswz<NCH>(key)) << 4)) = st.k[i];
-        if constexpr (WITH_V)
-            *reinterpret_cast<u32x4 *>(lv + key * ROW + ((ch ^ vswz<NCH>(key)) << 4)) = st.v[i];
-    }
-}
-
 template <int D, int RT, bool CROSS>
-__global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a)
+__global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnArgs a)
 {
     constexpr int KS = D / 32;                 // MFMA k-steps along d
     constexpr int DT = D / 16;                 // output d tiles
     constexpr int NCH = D / 8;                 // 16-byte chunks per row
     constexpr int ROW = 2 * D;                 // LDS bytes per K or V row
     constexpr int TILE = kKeyTile * ROW;       // LDS bytes per K (or V) tile
-    constexpr int SLD = TILE / (kThreads * 16);  // staged chunks per thread (K or V)
-    static_assert(kKeyTile == 32 && SLD >= 1, "tile geometry");
+    static_assert(kKeyTile == 32, "tile geometry");
+    const Stager<NCH, false, kThreads> stg1(threadIdx.x);
+    const Stager<NCH, true, kThreads> stg2(threadIdx.x);
 
     __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
     __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE];
@@ -234,23 +143,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
     if (n_kt > 0) {
         TileSR cur = to_sr(desc(0));
         uint32_t nraw = desc(1);
-        stage_store<NCH, SLD, false>(stage_load<NCH, SLD, false>(cur, it.kv_head, tid), lds_k[0], lds_v[0], tid);
+        stg1.store(stg1.load(cur, it.kv_head), lds_k[0], lds_v[0]);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
             const bool more = tt + 1 < n_kt;
             const TileSR nxt = to_sr(nraw);
             nraw = desc(tt + 2);
-            Staged<SLD> st;
+            Staged<NCH, false, kThreads> st;
             if (more)
-                st = stage_load<NCH, SLD, false>(nxt, it.kv_head, tid);
+                st = stg1.load(nxt, it.kv_head);
             const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
             if (need_mask)
                 sweep1_tile(cur, buf, std::true_type{});
             else
                 sweep1_tile(cur, buf, std::false_type{});
             if (more)
-                stage_store<NCH, SLD, false>(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+                stg1.store(st, lds_k[buf ^ 1], lds_v[buf ^ 1]);
             __syncthreads();
             cur = nxt;
         }
@@ -360,16 +269,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
     if (n_kt > 0) {
         TileSR cur = to_sr(desc(0)), prev = cur;
         uint32_t nraw = desc(1);
-        stage_store<NCH, SLD, true>(stage_load<NCH, SLD, true>(cur, it.kv_head, tid), lds_k[0], lds_v[0], tid);
+        stg2.store(stg2.load(cur, it.kv_head), lds_k[0], lds_v[0]);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
             const bool more = tt + 1 < n_kt;
             const TileSR nxt = to_sr(nraw);
             nraw = desc(tt + 2);
-            Staged<SLD> st;
+            Staged<NCH, true, kThreads> st;
             if (more)
-                st = stage_load<NCH, SLD, true>(nxt, it.kv_head, tid);
+                st = stg2.load(nxt, it.kv_head);
             if (tt > 0)
                 flush_impact(tt - 1, prev, buf ^ 1);
             const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
@@ -378,7 +287,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
             else
                 sweep2_tile(cur, buf, std::false_type{});
             if (more)
-                stage_store<NCH, SLD, true>(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+                stg2.store(st, lds_k[buf ^ 1], lds_v[buf ^ 1]);
             __syncthreads();
             prev = cur;
             cur = nxt;
@@ -409,37 +318,37 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(const AttnArgs a
 }
 
 template <int D, int RT>
-static void launch_rt(const AttnArgs &args, int n_items, hipStream_t stream)
+static void launch_wave_rt(const AttnArgs &args, int n_items, hipStream_t stream)
 {
-    if constexpr (RT <= kMaxRowTilesCross) {
+    if constexpr (RT <= kWaveMaxRowTilesCross) {
         if (args.cross) {
-            hipLaunchKernelGGL((attn_bf16_kernel<D, RT, true>), dim3(n_items), dim3(kThreads), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, true>), dim3(n_items), dim3(kThreads), 0, stream, args);
             return;
         }
     }
-    hipLaunchKernelGGL((attn_bf16_kernel<D, RT, false>), dim3(n_items), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, false>), dim3(n_items), dim3(kThreads), 0, stream, args);
 }
 
-hipError_t launch_attn_bf16(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream)
+hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream)
 {
     if (n_items <= 0)
         return hipSuccess;
-    if (args.cross && rt > kMaxRowTilesCross)
+    if (args.cross && rt > kWaveMaxRowTilesCross)
         return hipErrorInvalidValue;   // no such build; the planner never asks for it
     if (d == 128) {
         if (rt == 7)
-            launch_rt<128, 7>(args, n_items, stream);
+            launch_wave_rt<128, 7>(args, n_items, stream);
         else if (rt == 5)
-            launch_rt<128, 5>(args, n_items, stream);
+            launch_wave_rt<128, 5>(args, n_items, stream);
         else
-            launch_rt<128, 4>(args, n_items, stream);
+            launch_wave_rt<128, 4>(args, n_items, stream);
     } else {
         if (rt == 7)
-            launch_rt<64, 7>(args, n_items, stream);
+            launch_wave_rt<64, 7>(args, n_items, stream);
         else if (rt == 5)
-            launch_rt<64, 5>(args, n_items, stream);
+            launch_wave_rt<64, 5>(args, n_items, stream);
         else
-            launch_rt<64, 4>(args, n_items, stream);
+            launch_wave_rt<64, 4>(args, n_items, stream);
     }
     return hipGetLastError();
 }

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -23,7 +24,8 @@
 #include "crkv_internal.h"
 
 namespace crkv {
-hipError_t launch_attn_bf16(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_bf16_pair(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
 hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
@@ -235,7 +237,8 @@ struct Plan {
     size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0;
     size_t table_bytes = 0, off_partial = 0, total_bytes = 0;
     int max_keys = 0;
-    int rt = 1;   // row tiles per wave of the launch
+    int rt = 1;                 // row tiles per wave (wave kernel) or wave pair (pair kernel)
+    int kernel = kBf16Wave;     // bf16 kernel of the launch
 };
 
 int64_t packed_rows(const crkv_problem &p, int G, int mode)
@@ -246,31 +249,56 @@ int64_t packed_rows(const crkv_problem &p, int G, int mode)
     return (int64_t)G * (mode == CRKV_IMPACT_QUERY_ROWS ? p.q_len : n);
 }
 
-// Row tiles per wave for a bf16 launch. The matrix cores and the vector ALU
-// of a SIMD do not overlap on gfx950, and a workgroup takes as long as its
-// fullest wave, so:
-//  * if every (problem, KV head) fits in one workgroup, take the smallest
-//    build that covers the largest one (least padding, K/V read once);
-//  * otherwise take kRowTilesMany, the build measured fastest when the rows
-//    of a KV head span several workgroups (ragged and cross-document
-//    workloads on MI355X).
-// CRKV_ROW_TILES forces one of the built choices (tuning experiments).
-int choose_rt(const crkv_problem *problems, int n_problems, int G, int mode)
+// The bf16 kernel and its row tiles per wave (or wave pair) for a launch.
+// Every workgroup runs kWaves * rt row tiles per key tile whether or not they
+// are all real rows; its cost per key step is modelled as fixed + per_tile * rt
+// SIMD cycles (measured per kernel), and its key steps as the key tiles up to
+// its last row. The choice minimises the modelled sum over all workgroups.
+// CRKV_BF16_KERNEL (wave | pair) and CRKV_ROW_TILES force a built choice
+// (tuning experiments and tests).
+void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, int &kernel, int &rt)
 {
-    const int max_rt = mode == CRKV_IMPACT_CROSS_DOC ? kMaxRowTilesCross : 1 << 30;
-    if (const char *env = getenv("CRKV_ROW_TILES")) {
-        const int forced = atoi(env);
-        for (int rt : kRowTileChoices)
-            if (rt == forced && rt <= max_rt)
-                return rt;
+    const char *ek = getenv("CRKV_BF16_KERNEL");
+    const char *er = getenv("CRKV_ROW_TILES");
+    const int forced_rt = er ? atoi(er) : 0;
+    int64_t best_cost = INT64_MAX;
+    kernel = kBf16Pair;
+    rt = kPairRowTiles[0];
+    for (int k = kBf16Wave; k <= kBf16Pair; ++k) {
+        if (ek && strcmp(ek, k == kBf16Wave ? "wave" : "pair") != 0)
+            continue;
+        const int *choices = k == kBf16Wave ? kWaveRowTiles : kPairRowTiles;
+        const int64_t fixed = k == kBf16Wave ? kWaveStepFixed : kPairStepFixed;
+        const int64_t per = k == kBf16Wave ? kWaveStepPerTile : kPairStepPerTile;
+        for (int c = 0; c < 3; ++c) {
+            const int r = choices[c];
+            if (forced_rt && r != forced_rt)
+                continue;
+            if (k == kBf16Wave && mode == CRKV_IMPACT_CROSS_DOC && r > kWaveMaxRowTilesCross)
+                continue;
+            const int64_t cap = (int64_t)kWaves * r;
+            int64_t steps = 0;
+            for (int i = 0; i < n_problems; ++i) {
+                const crkv_problem &p = problems[i];
+                int64_t n_doc = 0;
+                for (int j = 0; j < p.m; ++j)
+                    n_doc += p.chunk_len[j];
+                const int64_t packed = packed_rows(p, G, mode);
+                const int64_t nrt = (packed + kRowTile - 1) / kRowTile;
+                const int64_t pos0 = mode == CRKV_IMPACT_QUERY_ROWS ? n_doc : 0;
+                for (int64_t tb = 0; tb < nrt; tb += cap) {
+                    const int64_t last_row = std::min(packed, (tb + cap) * kRowTile) - 1;
+                    steps += (pos0 + last_row / G + kKeyTile) / kKeyTile;
+                }
+            }
+            const int64_t cost = steps * (fixed + per * r);
+            if (cost <= best_cost) {   // ties go to the later (larger) build
+                best_cost = cost;
+                kernel = k;
+                rt = r;
+            }
+        }
     }
-    int64_t max_tiles = 0;
-    for (int i = 0; i < n_problems; ++i)
-        max_tiles = std::max<int64_t>(max_tiles, (packed_rows(problems[i], G, mode) + kRowTile - 1) / kRowTile);
-    for (int rt : kRowTileChoices)
-        if (rt <= max_rt && (int64_t)kWaves * rt >= max_tiles)
-            return rt;
-    return std::min(kRowTilesMany, max_rt);
 }
 
 // Builds the plan for a validated batch. Work items are ordered so that the
@@ -282,7 +310,10 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
 {
     const int G = H / H_kv;
     const bool bf16 = o.dtype == CRKV_BF16;
-    pl.rt = bf16 ? choose_rt(problems, n_problems, G, o.mode) : 1;
+    if (bf16)
+        choose_bf16(problems, n_problems, G, o.mode, pl.kernel, pl.rt);
+    else
+        pl.rt = 1;
     const int cap = bf16 ? kWaves * pl.rt : 1;   // row tiles per workgroup
     struct Group {
         int64_t cost;
@@ -513,6 +544,23 @@ size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, 
     return pl.total_bytes;
 }
 
+int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                   const crkv_opts *opts, int *kernel, int *row_tiles, int *workgroups)
+{
+    if (!kernel || !row_tiles || !workgroups)
+        return fail(CRKV_E_INVAL, "crkv_plan_info: NULL output pointer");
+    const crkv_opts o = resolve(opts);
+    const int rc = validate_batch(problems, n_problems, H, H_kv, d, o);
+    if (rc)
+        return rc;
+    Plan pl;
+    build_plan(pl, problems, n_problems, H, H_kv, d, o);
+    *kernel = o.dtype != CRKV_BF16 ? 0 : pl.kernel == kBf16Wave ? 1 : 2;
+    *row_tiles = pl.rt;
+    *workgroups = (int)pl.items.size();
+    return CRKV_OK;
+}
+
 int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                              const crkv_opts *opts)
 {
@@ -549,8 +597,9 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
     if (o.timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
     if (e == hipSuccess)
-        e = o.dtype == CRKV_BF16 ? launch_attn_bf16(d, pl.rt, args, (int)pl.items.size(), stream)
-                                 : launch_attn_f32(d, args, (int)pl.items.size(), stream);
+        e = o.dtype != CRKV_BF16      ? launch_attn_f32(d, args, (int)pl.items.size(), stream)
+            : pl.kernel == kBf16Wave ? launch_attn_bf16_wave(d, pl.rt, args, (int)pl.items.size(), stream)
+                                     : launch_attn_bf16_pair(d, pl.rt, args, (int)pl.items.size(), stream);
     if (e == hipSuccess && o.timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
     if (e == hipSuccess)

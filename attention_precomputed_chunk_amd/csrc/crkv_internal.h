@@ -10,13 +10,22 @@
 
 namespace crkv {
 
-constexpr int kWaves = 4;          // waves per workgroup (one per SIMD)
+constexpr int kWaves = 4;          // SIMDs per CU: row groups per bf16 workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 32;       // keys staged per LDS tile
 constexpr int kRowTile = 16;       // rows per MFMA row tile
-constexpr int kRowTileChoices[3] = {4, 5, 7};   // row tiles per wave the bf16 kernels are built for
-constexpr int kMaxRowTilesCross = 5;            // cross-document kernels: 7 would spill
-constexpr int kRowTilesMany = 5;                // when a KV head's rows span several workgroups
+// bf16 kernels. "wave": one wave per SIMD holds every role of its row tiles
+// (4 waves per workgroup). "pair": a producer and a consumer wave per SIMD
+// (8 waves per workgroup). Either way a workgroup covers kWaves * rt row tiles
+// of one KV head.
+enum Bf16Kernel { kBf16Wave = 0, kBf16Pair = 1 };
+constexpr int kWaveRowTiles[3] = {4, 5, 7};     // rt the wave kernels are built for
+constexpr int kWaveMaxRowTilesCross = 5;        // cross-document wave kernels: 7 would spill
+constexpr int kPairRowTiles[3] = {2, 4, 6};     // rt the pair kernels are built for
+// Planner cost model, SIMD cycles per 32-key step of one workgroup: a fixed
+// part and a part per row tile (fitted to measurements on MI355X).
+constexpr int kWaveStepFixed = 1884, kWaveStepPerTile = 778;
+constexpr int kPairStepFixed = 3166, kPairStepPerTile = 402;
 constexpr int kRowTilesF32 = 4;    // row tiles per wave, fp32 kernels
 constexpr int kTopkMaxK = 8192;    // selection buffer held in LDS
 

@@ -60,7 +60,8 @@ def algorithmic_work(wl):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "device_util.h", "crkv_internal.h"):
+    for f in ("attn_bf16_wave.hip", "attn_bf16_pair.hip", "attn_bf16_common.h", "device_util.h",
+              "crkv_internal.h", "crkv_api.hip"):
         with open(os.path.join(ROOT, "attention_precomputed_chunk_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -184,6 +185,8 @@ def main():
     imps = [pr["impact"] for pr in problems]
     torch.cuda.synchronize()
 
+    plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    log("plan: %s" % plan)
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
 
@@ -218,7 +221,8 @@ def main():
     traffic = measured_traffic(args.config)
     hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-           "kernel": "attn_bf16_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
+           "kernel": "attn_%s_kernel" % plan["kernel"], "row_tiles": plan["row_tiles"],
+           "workgroups": plan["workgroups"],
            "kernel_ms": round(k_ms, 4), "alg_bytes_per_launch": nbytes}
     mfma = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4),

@@ -150,6 +150,15 @@ int64_t crkv_budget(int64_t n_doc, double r);
 size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                            const crkv_opts *opts);
 
+/* The launch configuration crkv_attn_chunks_batched would use for these
+ * arguments: *kernel = 0 for the fp32 kernel, 1 for the bf16 kernel with one
+ * wave per SIMD, 2 for the bf16 kernel with producer/consumer wave pairs;
+ * *row_tiles = 16-row tiles per wave (or wave pair), *workgroups = grid size.
+ * Host-only (no device work); for inspection and tuning. Returns CRKV_OK, or
+ * CRKV_E_INVAL for invalid arguments or NULL outputs. */
+int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                   const crkv_opts *opts, int *kernel, int *row_tiles, int *workgroups);
+
 const char *crkv_status_string(int status);
 const char *crkv_last_error(void);
 int crkv_version(void);

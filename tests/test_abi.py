@@ -130,3 +130,37 @@ def test_batched_rejects_empty_batch(crkv_lib):
     crkv_lib.crkv_opts_init(ctypes.byref(o))
     assert crkv_lib.crkv_attn_chunks_batched(None, 0, 4, 4, 64, ctypes.byref(o)) == -1
     assert crkv_lib.crkv_attn_chunks_batched(None, 1, 4, 4, 64, ctypes.byref(o)) == -1
+
+
+def _fake_problem(doc_lens, q_len, H, d):
+    """Problem dict with placeholder device addresses (the planner never
+    dereferences them)."""
+    m = len(doc_lens)
+    return dict(Q=0x10000, chunk_K=[0x20000 + 0x1000 * i for i in range(m + 1)],
+                chunk_V=[0x40000 + 0x1000 * i for i in range(m + 1)], chunk_len=list(doc_lens) + [q_len],
+                q_len=q_len, out=0x60000, impact=0x70000)
+
+
+def test_plan_info_picks_kernel_by_shape(monkeypatch):
+    """Host-only: 25 packed row tiles per KV head fit one one-wave workgroup
+    (4 x 7 tiles); thousands of rows go to the wave-pair kernel."""
+    monkeypatch.delenv("CRKV_BF16_KERNEL", raising=False)
+    monkeypatch.delenv("CRKV_ROW_TILES", raising=False)
+    few = [_fake_problem([2500] * 4, 100, 32, 128) for _ in range(4)]
+    p = crkv.crkv_plan_info(few, 32, 8, 128, mode="query", dtype=crkv.CRKV_BF16)
+    assert p == {"kernel": "bf16_wave", "row_tiles": 7, "workgroups": 4 * 8}
+    many = [_fake_problem([3000, 3000], 1000, 64, 128)]
+    p = crkv.crkv_plan_info(many, 64, 8, 128, mode="query", dtype=crkv.CRKV_BF16)
+    assert p["kernel"] == "bf16_pair" and p["row_tiles"] == 6
+    p = crkv.crkv_plan_info(many, 64, 8, 128, mode="query", dtype=crkv.CRKV_F32)
+    assert p["kernel"] == "f32"
+    monkeypatch.setenv("CRKV_BF16_KERNEL", "wave")
+    monkeypatch.setenv("CRKV_ROW_TILES", "5")
+    p = crkv.crkv_plan_info(many, 64, 8, 128, mode="cross", dtype=crkv.CRKV_BF16)
+    assert p["kernel"] == "bf16_wave" and p["row_tiles"] == 5
+
+
+def test_plan_info_rejects_invalid():
+    bad = [_fake_problem([64], 16, 6, 128)]
+    with pytest.raises(crkv.CrkvError):
+        crkv.crkv_plan_info(bad, 6, 4, 128, mode="query", dtype=crkv.CRKV_BF16)   # H % H_kv != 0

@@ -98,6 +98,29 @@ def test_small_shapes(case):
     run_and_compare(wl, label="small%d" % case)
 
 
+# Every built bf16 (kernel, row tiles) configuration, forced through the
+# planner's override, on shapes whose rows span several workgroups.
+FORCED_BUILDS = [("wave", 4), ("wave", 5), ("wave", 7), ("pair", 2), ("pair", 4), ("pair", 6)]
+FORCED_CASES = [2, 3, 4, 5, 8]   # indices into SMALL: GQA query rows, cross (d=128, d=64), all rows, G=8
+
+
+@pytest.mark.parametrize("build", FORCED_BUILDS, ids=["%s%d" % b for b in FORCED_BUILDS])
+@pytest.mark.parametrize("case", FORCED_CASES)
+def test_forced_bf16_builds(case, build, monkeypatch):
+    seed, doc, q, H, H_kv, d, dtype, mode = SMALL[case]
+    kernel, rt = build
+    if kernel == "wave" and mode == "cross" and rt > 5:
+        pytest.skip("no cross-document wave build with 7 row tiles")
+    monkeypatch.setenv("CRKV_BF16_KERNEL", kernel)
+    monkeypatch.setenv("CRKV_ROW_TILES", str(rt))
+    say("forced", kernel, rt, "small case", SMALL[case])
+    wl = workloads.custom(100 + seed, doc, q, H, H_kv, d, dtype=dtype, mode=mode, r=0.1, n_problems=2)
+    dw = DeviceWorkload(wl)
+    plan = crkv.crkv_plan_info(dw.problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    assert plan["kernel"] == "bf16_" + kernel and plan["row_tiles"] == rt, plan
+    run_and_compare(wl, label="forced-%s%d-small%d" % (kernel, rt, case))
+
+
 def test_tiny_config():
     """1 layer, 4 heads, d=64, fp32; 2 chunks x 64 + 16 query rows; top-12."""
     say("tiny")
