@@ -81,6 +81,7 @@ struct Staged {
 
 // A thread's fixed part of the staging: which chunk it moves and where the
 // chunk lands in a tile buffer (the swizzled LDS byte offset), computed once.
+// WITH_V stages K then V of one tile; otherwise K alone.
 template <int NCH, bool WITH_V, int NT>
 struct Stager {
     using S = Staged<NCH, WITH_V, NT>;
@@ -133,23 +134,6 @@ struct Stager {
                 *reinterpret_cast<u32x4 *>((is_v(i) ? lv : lk) + lds[i]) = st.c[i];
     }
 };
-
-// Tiles t + 1 .. t + DEPTH in flight from global memory while tile t is in
-// use: a tile's loads are issued DEPTH steps before its LDS store, so the
-// memory latency is covered by DEPTH steps of work rather than one. Slots
-// shift down by one per step (static indices keep them in registers).
-template <int NCH, bool WITH_V, int NT, int DEPTH>
-struct Ring {
-    Staged<NCH, WITH_V, NT> s[DEPTH];
-};
-
-template <int NCH, bool WITH_V, int NT, int DEPTH>
-__device__ __forceinline__ void ring_shift(Ring<NCH, WITH_V, NT, DEPTH> &r)
-{
-#pragma unroll
-    for (int i = 0; i + 1 < DEPTH; ++i)
-        r.s[i] = r.s[i + 1];
-}
 
 // S^T of one 16-row tile against the two 16-key subtiles of a key tile.
 struct Spair {

@@ -24,7 +24,8 @@
 // matrix work, but cannot each hold Q, K and V fragments and a d = 128 output
 // accumulator in 256 registers. The workgroup therefore has 8 waves (waves w
 // and w + 4 share a SIMD) with roles:
-//   * sweep 1: every wave takes RT/2 row tiles and computes their lse;
+//   * sweep 1: every wave takes RT/2 row tiles and computes their lse, two
+//     key tiles per barrier;
 //   * sweep 2: wave p < 4 (producer) holds Q of RT row tiles, computes S and
 //     p and the impact column sums, and writes P^T fragments (bf16) to LDS;
 //     wave p + 4 (consumer) holds the O accumulators of the same rows and
@@ -43,8 +44,6 @@
 
 namespace crkv {
 
-constexpr int kDepth1 = 2;                     // tiles in flight, sweep 1 (K only)
-constexpr int kDepth2 = 1;                     // tiles in flight, sweep 2 (K and V)
 
 template <int D, int RT, bool CROSS>
 __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnArgs a)
@@ -102,14 +101,14 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
             row_m[rt] = -INFINITY;
             row_l[rt] = 0.f;
         }
-        auto tile = [&](TileSR kt, int buf, auto mask_tag) {
+        auto tile = [&](TileSR kt, const unsigned char *kb, auto mask_tag) {
             constexpr bool MASK = decltype(mask_tag)::value;
             bf16x8 kf[2][KS];
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+                    kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(kb + k_off(sub, ks));
 #pragma unroll
             for (int rt = 0; rt < RT1; ++rt) {
                 Spair sc = scores<KS>(kf, qf[rt]);
@@ -127,34 +126,45 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
                 row_m[rt] = tmax;
             }
         };
-        using R1 = Ring<NCH, false, kWsThreads, kDepth1>;
-        const Stager<NCH, false, kWsThreads> stg(tid);
-        R1 ring;
-        stg.store(stg.load(to_sr(desc(0)), it.kv_head), lds_k[0], lds_v[0]);
-#pragma unroll
-        for (int i = 1; i < kDepth1; ++i)
-            if (i < n_kt)
-                ring.s[i - 1] = stg.load(to_sr(desc(i)), it.kv_head);
-        TileSR cur = to_sr(desc(0));
-        uint32_t craw = desc(1), sraw = desc(kDepth1);
-        __syncthreads();
-        for (int tt = 0; tt < n_kt; ++tt) {
-            const int buf = tt & 1;
-            const TileSR nxt = to_sr(craw);
-            craw = desc(tt + 2);
-            const TileSR stile = to_sr(sraw);
-            sraw = desc(tt + kDepth1 + 1);
-            if (tt + kDepth1 < n_kt)
-                ring.s[kDepth1 - 1] = stg.load(stile, it.kv_head);
-            if ((cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos))
-                tile(cur, buf, std::true_type{});
+        auto run_tile = [&](TileSR kt, const unsigned char *kb) {
+            if ((kt.n_valid < kKeyTile) || (kt.key0 + kt.n_valid - 1 > wave_min_pos))
+                tile(kt, kb, std::true_type{});
             else
-                tile(cur, buf, std::false_type{});
-            if (tt + 1 < n_kt)
-                stg.store(ring.s[0], lds_k[buf ^ 1], lds_v[0]);
-            ring_shift(ring);
+                tile(kt, kb, std::false_type{});
+        };
+        // Two key tiles per barrier. Step g scores tiles 2g and 2g + 1 from
+        // the buffers of its parity (sweep 2's lds_k[0..1] for even g, its
+        // lds_v[0..1] for odd g) while tiles 2g + 2 and 2g + 3 are loaded and
+        // then stored into the other parity's buffers.
+        auto sbuf = [&](int g, int j) -> unsigned char * { return (g & 1) ? lds_v[j] : lds_k[j]; };
+        const Stager<NCH, false, kWsThreads> stg(tid);
+        TileSR c0 = to_sr(desc(0)), c1 = to_sr(desc(1));
+        stg.store(stg.load(c0, it.kv_head), sbuf(0, 0), nullptr);
+        if (n_kt > 1)
+            stg.store(stg.load(c1, it.kv_head), sbuf(0, 1), nullptr);
+        uint32_t raw0 = desc(2), raw1 = desc(3);
+        __syncthreads();
+        const int n_steps = (n_kt + 1) / 2;
+        for (int g = 0; g < n_steps; ++g) {
+            const int ta = 2 * g + 2, tb = 2 * g + 3;   // tiles loaded during this step
+            const TileSR s0 = to_sr(raw0), s1 = to_sr(raw1);
+            raw0 = desc(ta + 2);
+            raw1 = desc(tb + 2);
+            Staged<NCH, false, kWsThreads> sa, sb;
+            if (ta < n_kt)
+                sa = stg.load(s0, it.kv_head);
+            if (tb < n_kt)
+                sb = stg.load(s1, it.kv_head);
+            run_tile(c0, sbuf(g, 0));
+            if (2 * g + 1 < n_kt)
+                run_tile(c1, sbuf(g, 1));
+            if (ta < n_kt)
+                stg.store(sa, sbuf(g + 1, 0), nullptr);
+            if (tb < n_kt)
+                stg.store(sb, sbuf(g + 1, 1), nullptr);
             __syncthreads();
-            cur = nxt;
+            c0 = s0;
+            c1 = s1;
         }
         // Combine the four lane groups of each row into its log2-domain lse;
         // padded rows get +inf so every weight they would produce is 0.
@@ -173,20 +183,13 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     // Step s (0 <= s <= n_kt): the producers score key tile s from lds_k[s & 1]
     // and write its P^T to lds_p[s & 1]; the consumers run P.V of tile s - 1
     // from lds_p[(s - 1) & 1] and lds_v[(s - 1) % 3] and flush its impact;
-    // the producers store tile s + 1 into lds_k[(s + 1) & 1], lds_v[(s + 1) % 3]
-    // (loaded kDepth2 steps earlier) and start the loads of tile s + kDepth2.
-    // Every read of a buffer ends before the barrier after which it is refilled.
+    // the producers load tile s + 1 from global memory and store it into
+    // lds_k[(s + 1) & 1], lds_v[(s + 1) % 3]. Every read of a buffer ends
+    // before the barrier after which it is refilled.
     constexpr int NTP = kWaves * 64;   // the producers stage the tiles of sweep 2
-    using R2 = Ring<NCH, true, NTP, kDepth2>;
-    R2 ring2;
     const Stager<NCH, true, NTP> stg2(tid & (NTP - 1));
-    if (wave < kWaves) {
+    if (wave < kWaves)
         stg2.store(stg2.load(to_sr(desc(0)), it.kv_head), lds_k[0], lds_v[0]);
-#pragma unroll
-        for (int i = 1; i < kDepth2; ++i)
-            if (i < n_kt)
-                ring2.s[i - 1] = stg2.load(to_sr(desc(i)), it.kv_head);
-    }
     __syncthreads();   // also publishes lds_lse
 
     const int pair = wave & (kWaves - 1);
@@ -253,15 +256,14 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
             }
         };
         TileSR cur = to_sr(desc(0));
-        uint32_t craw = desc(1), sraw = desc(kDepth2);
+        uint32_t craw = desc(1);
         int vb = 1;   // lds_v slot of tile s + 1
         for (int s = 0; s <= n_kt; ++s) {
             const TileSR nxt = to_sr(craw);
             craw = desc(s + 2);
-            const TileSR stile = to_sr(sraw);
-            sraw = desc(s + kDepth2 + 1);
-            if (s + kDepth2 < n_kt)
-                ring2.s[kDepth2 - 1] = stg2.load(stile, it.kv_head);
+            Staged<NCH, true, NTP> st;
+            if (s + 1 < n_kt)
+                st = stg2.load(nxt, it.kv_head);
             if (s < n_kt) {
                 if ((cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos))
                     tile(cur, s & 1, std::true_type{});
@@ -269,8 +271,7 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
                     tile(cur, s & 1, std::false_type{});
             }
             if (s + 1 < n_kt)
-                stg2.store(ring2.s[0], lds_k[(s + 1) & 1], lds_v[vb]);
-            ring_shift(ring2);
+                stg2.store(st, lds_k[(s + 1) & 1], lds_v[vb]);
             __syncthreads();
             cur = nxt;
             vb = vb == 2 ? 0 : vb + 1;
