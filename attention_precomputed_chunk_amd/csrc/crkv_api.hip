@@ -187,8 +187,8 @@ int check_problem(const crkv_problem &p, int idx, int H, int H_kv, int d, int mo
         return fail(CRKV_E_INVAL, "problem %d: m = %d < 0", idx, p.m);
     if (p.q_len < 1)
         return fail(CRKV_E_INVAL, "problem %d: q_len = %d < 1", idx, p.q_len);
-    if (p.chunk_len[p.m] != p.q_len)
-        return fail(CRKV_E_INVAL, "problem %d: chunk_len[m] = %d must equal q_len = %d", idx,
+    if (p.chunk_len[p.m] < p.q_len)
+        return fail(CRKV_E_INVAL, "problem %d: chunk_len[m] = %d is less than q_len = %d", idx,
                     p.chunk_len[p.m], p.q_len);
     int64_t n = 0;
     for (int c = 0; c <= p.m; ++c) {
@@ -280,12 +280,12 @@ void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, 
             int64_t steps = 0;
             for (int i = 0; i < n_problems; ++i) {
                 const crkv_problem &p = problems[i];
-                int64_t n_doc = 0;
-                for (int j = 0; j < p.m; ++j)
-                    n_doc += p.chunk_len[j];
+                int64_t n_keys = 0;
+                for (int j = 0; j <= p.m; ++j)
+                    n_keys += p.chunk_len[j];
                 const int64_t packed = packed_rows(p, G, mode);
                 const int64_t nrt = (packed + kRowTile - 1) / kRowTile;
-                const int64_t pos0 = mode == CRKV_IMPACT_QUERY_ROWS ? n_doc : 0;
+                const int64_t pos0 = mode == CRKV_IMPACT_QUERY_ROWS ? n_keys - p.q_len : 0;
                 for (int64_t tb = 0; tb < nrt; tb += cap) {
                     const int64_t last_row = std::min(packed, (tb + cap) * kRowTile) - 1;
                     steps += (pos0 + last_row / G + kKeyTile) / kKeyTile;
@@ -327,10 +327,10 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
         int32_t n_doc = 0;
         for (int c = 0; c < p.m; ++c)
             n_doc += p.chunk_len[c];
-        const int32_t N = n_doc + p.q_len;
+        const int32_t N = n_doc + p.chunk_len[p.m];
         const bool query = o.mode == CRKV_IMPACT_QUERY_ROWS;
         const int32_t rows = query ? p.q_len : N;
-        const int32_t pos0 = query ? n_doc : 0;
+        const int32_t pos0 = query ? N - p.q_len : 0;   // query rows are the last q_len positions
         pl.seg_base.push_back(pl.segs.size());
         pl.tile_base.push_back(pl.tiles.size());
         int32_t start = 0;

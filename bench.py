@@ -51,8 +51,8 @@ def algorithmic_work(wl):
         N = p.n_keys
         rows = p.q_len if wl.mode == "query" else N
         nbytes += N * 2 * wl.H_kv * wl.d * s + rows * 2 * wl.H * wl.d * s + N * 4
-        if wl.mode == "query":
-            pairs += p.q_len * p.n_doc + p.q_len * (p.q_len + 1) // 2
+        if wl.mode == "query":   # the q_len rows are the last positions
+            pairs += p.q_len * (N - p.q_len) + p.q_len * (p.q_len + 1) // 2
         else:
             pairs += N * (N + 1) // 2
     return nbytes, 4 * pairs * wl.H * wl.d, pairs

@@ -27,16 +27,20 @@
  *    reason (per thread).
  *  - Segment c of a problem stores K and V as [H_kv][chunk_len[c]][d],
  *    contiguous, in the element type opts->dtype. Entries 0..m-1 are document
- *    chunks (length 0 allowed: the chunk is skipped); entry m is the query
- *    block's own K/V and must have length q_len. Chunks are never copied or
+ *    chunks (length 0 allowed: the chunk is skipped); N_doc is their total
+ *    length. Entry m holds the query block's own K/V, chunk_len[m] >= q_len:
+ *    the q_len query rows are the last q_len positions of the concatenation,
+ *    and any earlier keys of entry m are tokens generated before them (a
+ *    decode step has q_len = 1 and a growing entry m). N = N_doc +
+ *    chunk_len[m] is the number of keys. Chunks are never copied or
  *    concatenated in memory: the library reads them through the pointer table.
  *  - Q and out are [H][rows][d] in opts->dtype. rows = q_len in
- *    CRKV_IMPACT_QUERY_ROWS mode, and N_doc + q_len (every position of the
- *    concatenated sequence) in the two all-position modes.
+ *    CRKV_IMPACT_QUERY_ROWS mode, and N (every position of the concatenated
+ *    sequence) in the two all-position modes.
  *  - Query head h reads KV head h / (H / H_kv).
- *  - impact is float32 [N_doc + q_len] (document keys first, then the query
- *    block's keys), overwritten, summed over all H query heads.
- *  - Supported: d in {64, 128}; H % H_kv == 0; N_doc + q_len < 2^31.
+ *  - impact is float32 [N] (document keys first, then entry m's keys),
+ *    overwritten, summed over all H query heads.
+ *  - Supported: d in {64, 128}; H % H_kv == 0; N < 2^30.
  */
 #ifndef CRKV_H
 #define CRKV_H
@@ -70,7 +74,7 @@ typedef enum { CRKV_F32 = 0, CRKV_BF16 = 1 } crkv_dtype;
  *              equation, index set read as doc(j) != doc(i); the query block
  *              is segment m). Same-segment rows still take part in softmax.
  *  ALL_ROWS:   every position is a row; impact sums every row (a check mode:
- *              the impact vector then sums to (N_doc + q_len) * H).
+ *              the impact vector then sums to N * H).
  */
 typedef enum {
     CRKV_IMPACT_QUERY_ROWS = 0,
@@ -97,9 +101,9 @@ void crkv_opts_init(crkv_opts *opts);
  * Attention of one problem over m document chunks plus the query block.
  *  Q          device, [H][rows][d]
  *  chunk_K/V  host arrays of m + 1 device pointers (see conventions)
- *  chunk_len  host array of m + 1 lengths; chunk_len[m] == q_len
+ *  chunk_len  host array of m + 1 lengths; chunk_len[m] >= q_len
  *  out        device, [H][rows][d], written
- *  impact     device, float32 [N_doc + q_len], written
+ *  impact     device, float32 [N], written
  *  opts       NULL for the defaults
  */
 int crkv_attn_chunks(const void *Q, const void *const *chunk_K, const void *const *chunk_V,

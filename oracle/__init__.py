@@ -24,9 +24,14 @@ MODE_CODE = {"query": 0, "cross": 1, "all": 2}
 DTYPE_CODE = {"f32": 0, "bf16": 1}
 
 
+def _stale() -> bool:
+    return not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (OpenMP, -O2)."""
-    if force or not os.path.exists(_LIB):
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, -O2); without
+    ``force``, only when the library is missing or older than the source."""
+    if force or _stale():
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
                         "-o", tmp, _SRC, "-lm"], check=True)
@@ -37,7 +42,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _stale():
             build()
         lib = ctypes.CDLL(_LIB)
         vp = ctypes.c_void_p

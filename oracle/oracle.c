@@ -64,8 +64,13 @@ static double widen(const void *base, int dtype, size_t i)
 /*
  * Attention of every row over the concatenated segments, plus impact.
  *
- * Q      [H][rows][d]; rows = q_len (query-row mode) or N_doc + q_len.
- * K, V   m + 1 pointers; segment c is [H_kv][lens[c]][d]; lens[m] == q_len.
+ * Q      [H][rows][d]; rows = q_len (query-row mode) or N = sum of lens.
+ * K, V   m + 1 pointers; segment c is [H_kv][lens[c]][d]; lens[m] >= q_len.
+ *        Segment m holds the query block's own keys: in query-row mode the
+ *        q_len rows are the last q_len positions of the concatenation (in a
+ *        decode step segment m also holds the earlier generated tokens, and
+ *        the one row is the newest token, which sees every key: TurboRAG
+ *        summary, the generation loop that appends each token's K/V).
  * causal 1: key i is visible to the row at position p iff pos(i) <= p.
  *        0: every key is visible (the listing's unmasked softmax).
  * row_lo, row_hi  only rows in [row_lo, row_hi) are computed (row_hi <= 0:
@@ -83,7 +88,7 @@ int oracle_attn(int dtype, int mode, int causal, const void *Q, const void *cons
                 int n_threads)
 {
     if (!Q || !K || !V || !lens || m < 0 || q_len < 1 || H < 1 || H_kv < 1 || d < 1 ||
-        H % H_kv != 0 || lens[m] != q_len)
+        H % H_kv != 0 || lens[m] < q_len)
         return -1;
     long n_doc = 0;
     for (int c = 0; c < m; ++c) {
@@ -91,7 +96,7 @@ int oracle_attn(int dtype, int mode, int causal, const void *Q, const void *cons
             return -1;
         n_doc += lens[c];
     }
-    const long N = n_doc + q_len;
+    const long N = n_doc + lens[m];
     const long rows = (mode == OR_QUERY_ROWS) ? q_len : N;
     if (row_hi <= 0 || row_hi > rows)
         row_hi = (int)rows;
@@ -152,7 +157,7 @@ int oracle_attn(int dtype, int mode, int causal, const void *Q, const void *cons
             const int h = (int)(task / n_rows_run);
             const long j = row_lo + task % n_rows_run;
             const int hk = h / G;
-            const long pos = (mode == OR_QUERY_ROWS) ? n_doc + j : j;
+            const long pos = (mode == OR_QUERY_ROWS) ? N - q_len + j : j;
             const int seg_row = seg_of[pos];
             const long n_vis = causal ? pos + 1 : N;
             const size_t qbase = ((size_t)h * (size_t)rows + (size_t)j) * (size_t)d;

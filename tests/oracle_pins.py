@@ -7,8 +7,9 @@ full-prefill formulation), the CacheBlend listing's unmasked softmax, closed
 forms for uniform attention, row-stochastic softmax, the impact mass, the
 invariance of concatenation under re-partitioning, GQA as MHA with repeated
 K/V heads, textbook causal attention when there are no documents, a single
-softmax row, a dominant key, a brute-force top-k on tiny inputs and the
-budget k = max(1, int(N_doc * r)).
+softmax row, a dominant key, decode steps (the newest token over a growing
+last segment) against torch and against the query block's rows, a
+brute-force top-k on tiny inputs and the budget k = max(1, int(N_doc * r)).
 
 Every pin is a function of an oracle module (``orc``), so that the
 planted-mistake test can run the same pins against a mutated copy of the
@@ -39,8 +40,8 @@ def torch_reference(prob, H, H_kv, d, dtype, mode, causal=True):
     V = torch.cat([_t(v, dtype) for v in prob.V], dim=1).repeat_interleave(G, dim=0)
     N = prob.n_keys
     seg_key = torch.cat([torch.full((n,), c) for c, n in enumerate(prob.lens)])
-    if mode == "query":
-        row_pos = prob.n_doc + torch.arange(prob.q_len)
+    if mode == "query":   # the q_len rows are the last positions of the concatenation
+        row_pos = N - prob.q_len + torch.arange(prob.q_len)
     else:
         row_pos = torch.arange(N)
     seg_row = seg_key[row_pos]
@@ -237,6 +238,53 @@ def pin_single_query_row_is_one_softmax(orc):
         close(out[h, 0], p @ Vc[h], atol=1e-13)
         close(lse[h, 0], s.max() + math.log(np.exp(s - s.max()).sum()), rtol=1e-14)
     close(imp.sum(), H, rtol=1e-14)
+
+
+def pin_decode_step_matches_torch_sdpa(orc):
+    """A decode step (TurboRAG summary, the generation loop that appends each
+    token's K/V): the last segment holds earlier generated tokens and the one
+    query row is the newest position, which sees every key."""
+    for seed, doc, gen, H, H_kv, d, dtype in [(31, [9, 0, 6], 5, 4, 2, 16, "f32"),
+                                              (32, [12], 3, 2, 1, 8, "bf16"),
+                                              (33, [], 7, 2, 2, 8, "f32")]:
+        wl = workloads.custom(seed, doc, 1, H, H_kv, d, dtype=dtype, gen_len=gen)
+        prob = wl.problems[0]
+        assert prob.lens[-1] == gen + 1
+        out, imp, _ = orc.attn(prob, H, H_kv, d, dtype, "query")
+        ref_out, ref_imp = torch_reference(prob, H, H_kv, d, dtype, "query")
+        close(out, ref_out, atol=1e-12)
+        close(imp, ref_imp, atol=1e-12)
+
+
+def pin_uniform_decode_closed_form(orc):
+    """Q = 0 in a decode step: every key gets weight 1/N, so the output is the
+    mean of all V rows of the head's KV head and every impact is H / N."""
+    doc, gen, H, H_kv, d = [5, 3], 4, 4, 2, 8
+    wl = workloads.custom(34, doc, 1, H, H_kv, d, gen_len=gen)
+    prob = wl.problems[0]
+    prob.Q[...] = 0
+    out, imp, _ = orc.attn(prob, H, H_kv, d, "f32", "query")
+    N = prob.n_keys
+    close(imp, np.full(N, H / N), rtol=1e-13)
+    Vcat = np.concatenate([v.astype(np.float64) for v in prob.V], axis=1)
+    for h in range(H):
+        close(out[h, 0], Vcat[h // (H // H_kv)].mean(axis=0), atol=1e-13)
+
+
+def pin_prefill_rows_equal_decode_steps(orc):
+    """Causality: row j of a T-row query block sees exactly the keys a decode
+    step sees when the last segment stops at that row's own key."""
+    doc, T, H, d = [6, 4], 5, 2, 8
+    wl = workloads.custom(35, doc, T, H, H, d)
+    prob = wl.problems[0]
+    out, _, _ = orc.attn(prob, H, H, d, "f32", "query")
+    for j in range(T):
+        step = workloads.Problem(K=prob.K[:-1] + [np.ascontiguousarray(prob.K[-1][:, : j + 1])],
+                                 V=prob.V[:-1] + [np.ascontiguousarray(prob.V[-1][:, : j + 1])],
+                                 lens=prob.lens[:-1] + [j + 1], q_len=1,
+                                 Q=np.ascontiguousarray(prob.Q[:, j : j + 1]))
+        o1, _, _ = orc.attn(step, H, H, d, "f32", "query")
+        close(o1[:, 0], out[:, j], atol=1e-14)
 
 
 def pin_dominant_key_takes_all_impact(orc):

@@ -16,7 +16,8 @@ SRC_DIR = os.path.dirname(os.path.abspath(oracle.__file__))
 MUTATIONS = {
     "scale_by_d": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),
     "mask_off_by_one": ("causal ? pos + 1 : N", "causal ? (pos + 2 < N ? pos + 2 : N) : N"),
-    "query_rows_at_start": ("(mode == OR_QUERY_ROWS) ? n_doc + j : j", "j"),
+    "query_rows_at_start": ("(mode == OR_QUERY_ROWS) ? N - q_len + j : j", "j"),
+    "query_rows_after_documents": ("(mode == OR_QUERY_ROWS) ? N - q_len + j : j", "(mode == OR_QUERY_ROWS) ? n_doc + j : j"),
     "gqa_modulo_groups": ("const int hk = h / G;", "const int hk = h % H_kv;"),
     "lse_sign": ("mx + log(l)", "mx - log(l)"),
     "unnormalised_weights": ("exp(s[i] - row_lse)", "exp(s[i] - mx)"),

@@ -19,7 +19,7 @@ Layouts (all C-contiguous):
   segments ``0..m-1`` are the document chunks, segment ``m`` is the query
   block's own K/V (TurboRAG eq. for K_combined places K^(Q) last).
 * ``Q`` is ``[H][rows][d]``: ``rows = q_len`` in query-row mode, and
-  ``rows = N_doc + q_len`` (every position) in the cross-document and all-rows
+  ``rows = N`` (every position, N = sum of lens) in the cross-document and all-rows
   modes.
 * bf16 tensors are stored as ``uint16`` bit patterns; fp32 as ``float32``.
 
@@ -111,7 +111,7 @@ class Problem:
 
     K: List[np.ndarray]
     V: List[np.ndarray]
-    lens: List[int]          # m + 1 entries, the last is q_len
+    lens: List[int]          # m + 1 entries; the last is gen_len + q_len (the query block's segment)
     q_len: int
     Q: np.ndarray
 
@@ -173,8 +173,10 @@ def ragged_shapes(spec: ConfigSpec):
 
 def make_problem(rng: np.random.Generator, doc_lens: Sequence[int], q_len: int, H: int,
                  H_kv: int, d: int, dtype: str, mode: str, k_outliers: int = 0,
-                 outlier_scale: float = 8.0) -> Problem:
-    lens = [int(x) for x in doc_lens] + [int(q_len)]
+                 outlier_scale: float = 8.0, gen_len: int = 0) -> Problem:
+    """gen_len earlier generated tokens precede the q_len query rows in the
+    last segment (a decode step: q_len = 1)."""
+    lens = [int(x) for x in doc_lens] + [int(gen_len) + int(q_len)]
     K32, V32 = [], []
     for n in lens:
         K32.append(rng.standard_normal((H_kv, n, d), dtype=np.float32))
@@ -212,14 +214,15 @@ def generate(name: str, problems: Optional[Sequence[int]] = None,
 
 def custom(seed: int, doc_lens: Sequence[int], q_len: int, H: int, H_kv: int, d: int,
            dtype: str = "f32", mode: str = "query", r: float = 0.1, n_problems: int = 1,
-           k_outliers: int = 0) -> Workload:
+           k_outliers: int = 0, gen_len: int = 0) -> Workload:
     """A small workload of arbitrary shape, for tests."""
     if mode not in MODES:
         raise ValueError(mode)
     wl = Workload(spec=None, H=H, H_kv=H_kv, d=d, dtype=dtype, mode=mode, r=r)
     for p in range(n_problems):
         rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(p,)))
-        wl.problems.append(make_problem(rng, doc_lens, q_len, H, H_kv, d, dtype, mode, k_outliers))
+        wl.problems.append(make_problem(rng, doc_lens, q_len, H, H_kv, d, dtype, mode, k_outliers,
+                                        gen_len=gen_len))
         wl.problem_ids.append(p)
     return wl
 
