@@ -10,6 +10,7 @@ Functions carry the C names:
 * ``crkv_attn_chunks(Q, chunk_K, chunk_V, chunk_len, m, q_len, H, H_kv, d, out, impact, ...)``
 * ``crkv_attn_chunks_batched(problems, H, H_kv, d, ...)``
 * ``crkv_topk(impact, n, k, idx, ...)`` and ``crkv_topk_batched(...)``
+* ``crkv_decode_chunks_batched(problems, H, H_kv, d, ...)`` (one decode step)
 * ``crkv_budget(n_doc, r)``, ``crkv_workspace_size(...)``, ``crkv_plan_info(...)``,
   ``crkv_version()``
 """
@@ -56,6 +57,7 @@ _lib = None
 
 DECLARED = ["crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
             "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
+            "crkv_decode_chunks_batched", "crkv_decode_workspace_size",
             "crkv_status_string", "crkv_last_error", "crkv_version"]
 
 
@@ -95,6 +97,12 @@ def lib():
                                      ctypes.POINTER(crkv_opts), ctypes.POINTER(c_int), ctypes.POINTER(c_int),
                                      ctypes.POINTER(c_int)]
         L.crkv_plan_info.restype = c_int
+        L.crkv_decode_chunks_batched.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                                 ctypes.POINTER(crkv_opts)]
+        L.crkv_decode_chunks_batched.restype = c_int
+        L.crkv_decode_workspace_size.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                                 ctypes.POINTER(crkv_opts)]
+        L.crkv_decode_workspace_size.restype = ctypes.c_size_t
         L.crkv_status_string.argtypes = [c_int]
         L.crkv_status_string.restype = ctypes.c_char_p
         L.crkv_last_error.argtypes = []
@@ -175,7 +183,7 @@ def crkv_attn_chunks(Q, chunk_K: Sequence, chunk_V: Sequence, chunk_len: Sequenc
 
 def _problems(problems):
     ps = [_Problem(pr["Q"], pr["chunk_K"], pr["chunk_V"], pr["chunk_len"], pr["q_len"], pr["out"],
-                   pr["impact"]) for pr in problems]
+                   pr.get("impact")) for pr in problems]
     arr = (crkv_problem * len(ps))(*[p.c for p in ps])
     return ps, arr
 
@@ -196,6 +204,21 @@ def crkv_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int, mod
     keep, arr = _problems(problems)
     o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream=0)
     return int(lib().crkv_workspace_size(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+def crkv_decode_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int, stream=None,
+                               workspace=None, workspace_bytes: int = 0, timing_events=None):
+    """One decode step (q_len = 1 per problem); dicts as for crkv_attn_chunks_batched,
+    'impact' may be None."""
+    keep, arr = _problems(problems)
+    o = make_opts(CRKV_BF16, "query", stream, workspace, workspace_bytes, timing_events)
+    _check(lib().crkv_decode_chunks_batched(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+def crkv_decode_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int) -> int:
+    keep, arr = _problems(problems)
+    o = make_opts(CRKV_BF16, "query", stream=0)
+    return int(lib().crkv_decode_workspace_size(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
 
 
 PLAN_KERNELS = {0: "f32", 1: "bf16_wave", 2: "bf16_pair"}

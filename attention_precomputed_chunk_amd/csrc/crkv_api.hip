@@ -26,6 +26,7 @@
 namespace crkv {
 hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_bf16_pair(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_decode_bf16(int d, const DecodeArgs &args, int n_items, int n_pairs, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
 hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
@@ -177,9 +178,9 @@ int check_opts(const crkv_opts &o)
     return CRKV_OK;
 }
 
-int check_problem(const crkv_problem &p, int idx, int H, int H_kv, int d, int mode)
+int check_problem(const crkv_problem &p, int idx, int H, int H_kv, int d, int mode, bool need_impact = true)
 {
-    if (!p.Q || !p.out || !p.impact)
+    if (!p.Q || !p.out || (need_impact && !p.impact))
         return fail(CRKV_E_INVAL, "problem %d: Q, out and impact must be non-null", idx);
     if (!p.chunk_K || !p.chunk_V || !p.chunk_len)
         return fail(CRKV_E_INVAL, "problem %d: chunk_K, chunk_V and chunk_len must be non-null", idx);
@@ -208,7 +209,7 @@ int check_problem(const crkv_problem &p, int idx, int H, int H_kv, int d, int mo
         return fail(CRKV_E_UNSUPPORTED, "problem %d: too many rows", idx);
     if (!aligned16(p.Q) || !aligned16(p.out))
         return fail(CRKV_E_INVAL, "problem %d: Q and out must be 16-byte aligned", idx);
-    if (reinterpret_cast<uintptr_t>(p.impact) & 3u)
+    if (need_impact && (reinterpret_cast<uintptr_t>(p.impact) & 3u))
         return fail(CRKV_E_INVAL, "problem %d: impact must be 4-byte aligned", idx);
     return CRKV_OK;
 }
@@ -497,6 +498,123 @@ int check_topk_args(const float *impact, int n, int k, const int32_t *idx, int w
 
 // ================================================================== C ABI
 
+// ------------------------------------------------------------ decode plan
+// Workgroups the split of a decode launch aims for (8 per CU of MI355X).
+constexpr int64_t kDecodeTargetItems = 8 * 256;
+
+struct DecodePlan {
+    std::vector<ProbDesc> probs;
+    std::vector<KTile> tiles;
+    std::vector<DecodeItem> items;
+    std::vector<DecodePair> pairs;
+    std::vector<size_t> tile_base;   // per problem
+    size_t off_probs = 0, off_items = 0, off_pairs = 0, off_tiles = 0;
+    size_t table_bytes = 0, off_part = 0, total_bytes = 0;
+    int split = 0;   // key tiles per range
+};
+
+int validate_decode(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                    const crkv_opts &o)
+{
+    int rc = check_opts(o);
+    if (rc)
+        return rc;
+    if (o.dtype != CRKV_BF16)
+        return fail(CRKV_E_UNSUPPORTED, "decode: only CRKV_BF16 is supported");
+    rc = check_shape(n_problems, H, H_kv, d);
+    if (rc)
+        return rc;
+    if (H / H_kv > kDecodeMaxGroup)
+        return fail(CRKV_E_UNSUPPORTED, "decode: H / H_kv = %d query heads per KV head exceed %d",
+                    H / H_kv, kDecodeMaxGroup);
+    if (!problems)
+        return fail(CRKV_E_INVAL, "problems must be non-null");
+    for (int i = 0; i < n_problems; ++i) {
+        if (problems[i].q_len != 1)
+            return fail(CRKV_E_INVAL, "decode problem %d: q_len = %d, must be 1", i, problems[i].q_len);
+        rc = check_problem(problems[i], i, H, H_kv, d, CRKV_IMPACT_QUERY_ROWS, false);
+        if (rc)
+            return rc;
+    }
+    return CRKV_OK;
+}
+
+// Key tiles of a problem (never straddling a segment) appended to `tiles`.
+void append_tiles(std::vector<KTile> &tiles, const crkv_problem &p, int d, size_t esz)
+{
+    int32_t start = 0;
+    for (int c = 0; c <= p.m; ++c) {
+        const int32_t len = p.chunk_len[c];
+        for (int32_t t = 0; t < len; t += kKeyTile) {
+            KTile kt;
+            kt.K = static_cast<const unsigned char *>(p.chunk_K[c]) + (size_t)t * d * esz;
+            kt.V = static_cast<const unsigned char *>(p.chunk_V[c]) + (size_t)t * d * esz;
+            kt.n_valid = std::min(kKeyTile, len - t);
+            kt.key0 = start + t;
+            kt.seg_len = len;
+            kt.seg_lo = start;
+            tiles.push_back(kt);
+        }
+        start += len;
+    }
+}
+
+// Splits every (problem, KV head) into ranges of `split` key tiles, with
+// `split` chosen so that the launch has about kDecodeTargetItems workgroups
+// (a multiple of the split kernel's 4 waves, at least 4 tiles, at most 256).
+void build_decode_plan(DecodePlan &pl, const crkv_problem *problems, int n_problems, int H, int H_kv,
+                       int d)
+{
+    const int G = H / H_kv;
+    int64_t all_tiles = 0;
+    pl.probs.resize(n_problems);
+    for (int pi = 0; pi < n_problems; ++pi) {
+        pl.tile_base.push_back(pl.tiles.size());
+        append_tiles(pl.tiles, problems[pi], d, 2);
+        all_tiles += (int64_t)(pl.tiles.size() - pl.tile_base.back()) * H_kv;
+    }
+    int64_t split = (all_tiles + kDecodeTargetItems - 1) / kDecodeTargetItems;
+    split = std::min<int64_t>(256, std::max<int64_t>(kDecodeWaves, split));
+    split = (split + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+    pl.split = (int)split;
+    for (int pi = 0; pi < n_problems; ++pi) {
+        const crkv_problem &p = problems[pi];
+        const int n_tiles = (int)((pi + 1 < n_problems ? pl.tile_base[pi + 1] : pl.tiles.size()) - pl.tile_base[pi]);
+        int32_t n_keys = 0;
+        for (int c = 0; c <= p.m; ++c)
+            n_keys += p.chunk_len[c];
+        ProbDesc &pd = pl.probs[pi];
+        memset(&pd, 0, sizeof pd);
+        pd.n_tiles = n_tiles;
+        pd.n_seg = p.m + 1;
+        pd.n_keys = n_keys;
+        pd.rows = 1;
+        pd.pos0 = n_keys - 1;
+        for (int kv = 0; kv < H_kv; ++kv) {
+            DecodePair pp{pi, kv, (int32_t)pl.items.size(), 0};
+            for (int tb = 0; tb < n_tiles; tb += pl.split) {
+                DecodeItem it{};
+                it.prob = pi;
+                it.kv_head = kv;
+                it.tile_begin = tb;
+                it.n_tiles = std::min(pl.split, n_tiles - tb);
+                it.part = (int32_t)pl.items.size();
+                pl.items.push_back(it);
+                ++pp.n_parts;
+            }
+            pl.pairs.push_back(pp);
+        }
+    }
+    pl.off_probs = 0;
+    pl.off_items = align_up(pl.off_probs + pl.probs.size() * sizeof(ProbDesc), 256);
+    pl.off_pairs = align_up(pl.off_items + pl.items.size() * sizeof(DecodeItem), 256);
+    pl.off_tiles = align_up(pl.off_pairs + pl.pairs.size() * sizeof(DecodePair), 256);
+    pl.table_bytes = align_up(pl.off_tiles + pl.tiles.size() * sizeof(KTile), 256);
+    pl.off_part = pl.table_bytes;
+    pl.total_bytes = pl.off_part + pl.items.size() * (size_t)G * (2 + d) * sizeof(float);
+    (void)H;
+}
+
 extern "C" {
 
 void crkv_opts_init(crkv_opts *opts)
@@ -511,6 +629,68 @@ void crkv_opts_init(crkv_opts *opts)
 int crkv_version(void) { return CRKV_VERSION; }
 
 const char *crkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t crkv_decode_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                                  const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    if (validate_decode(problems, n_problems, H, H_kv, d, o) != CRKV_OK)
+        return 0;
+    DecodePlan pl;
+    build_decode_plan(pl, problems, n_problems, H, H_kv, d);
+    return pl.total_bytes;
+}
+
+int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                               const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = validate_decode(problems, n_problems, H, H_kv, d, o);
+    if (rc)
+        return rc;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    DecodePlan pl;
+    build_decode_plan(pl, problems, n_problems, H, H_kv, d);
+    Scratch sc;
+    rc = scratch_get(sc, pl.total_bytes, o, stream);
+    if (rc)
+        return rc;
+    unsigned char *dev = static_cast<unsigned char *>(sc.ptr);
+    for (int pi = 0; pi < n_problems; ++pi) {
+        ProbDesc &pd = pl.probs[pi];
+        pd.Q = problems[pi].Q;
+        pd.out = problems[pi].out;
+        pd.tiles = reinterpret_cast<const KTile *>(dev + pl.off_tiles) + pl.tile_base[pi];
+    }
+    std::vector<unsigned char> host(pl.table_bytes, 0);
+    memcpy(host.data() + pl.off_probs, pl.probs.data(), pl.probs.size() * sizeof(ProbDesc));
+    memcpy(host.data() + pl.off_items, pl.items.data(), pl.items.size() * sizeof(DecodeItem));
+    memcpy(host.data() + pl.off_pairs, pl.pairs.data(), pl.pairs.size() * sizeof(DecodePair));
+    memcpy(host.data() + pl.off_tiles, pl.tiles.data(), pl.tiles.size() * sizeof(KTile));
+    rc = staged_upload(dev, host.data(), pl.table_bytes, stream);
+    if (rc) {
+        scratch_release(sc, stream);
+        return rc;
+    }
+    DecodeArgs args{};
+    args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
+    args.items = reinterpret_cast<const DecodeItem *>(dev + pl.off_items);
+    args.pairs = reinterpret_cast<const DecodePair *>(dev + pl.off_pairs);
+    args.part = reinterpret_cast<float *>(dev + pl.off_part);
+    args.G = H / H_kv;
+    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    hipError_t e = hipSuccess;
+    if (o.timing_events[0])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
+    if (e == hipSuccess)
+        e = launch_decode_bf16(d, args, (int)pl.items.size(), (int)pl.pairs.size(), stream);
+    if (e == hipSuccess && o.timing_events[1])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    scratch_release(sc, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode launch");
+    return CRKV_OK;
+}
 
 const char *crkv_status_string(int status)
 {

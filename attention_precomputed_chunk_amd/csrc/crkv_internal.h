@@ -62,7 +62,7 @@ struct ProbDesc {
     int32_t n_doc;
     int32_t n_keys;
     int32_t rows;           // rows per head
-    int32_t pos0;           // position of row 0 (N_doc in query-row mode, else 0)
+    int32_t pos0;           // position of row 0 (N - q_len in query-row mode, else 0)
     int32_t n_slots;
     int32_t pad;
 };
@@ -82,6 +82,38 @@ struct AttnArgs {
     const ItemDesc *items;
     int32_t H, H_kv, G;
     int32_t cross;          // 1: impact skips rows of the key's own segment
+    float c_log2;           // log2(e) / sqrt(d)
+};
+
+// Decode step (q_len = 1): the keys of each (problem, KV head) are split into
+// ranges of key tiles; one workgroup per range writes a partial softmax state
+// (per query head of the group: running max, sum, unnormalised output row),
+// and one workgroup per (problem, KV head) merges the ranges in order.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeMaxGroup = 16;    // query heads per KV head (one 16-row MFMA tile)
+
+struct DecodeItem {
+    int32_t prob;
+    int32_t kv_head;
+    int32_t tile_begin;     // first key tile of the range (index into the problem's list)
+    int32_t n_tiles;
+    int32_t part;           // partial slot of the range
+    int32_t pad0, pad1, pad2;
+};
+
+struct DecodePair {
+    int32_t prob;
+    int32_t kv_head;
+    int32_t part_begin;     // the pair's ranges occupy slots [part_begin, part_begin + n_parts)
+    int32_t n_parts;
+};
+
+struct DecodeArgs {
+    const ProbDesc *probs;
+    const DecodeItem *items;
+    const DecodePair *pairs;
+    float *part;            // per slot: G x (max, sum) then G x d unnormalised output
+    int32_t G;
     float c_log2;           // log2(e) / sqrt(d)
 };
 

@@ -11,6 +11,9 @@ document tokens + 100 query tokens, r = 0.15), the shape of TurboRAG's
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 
+With --config llama3_8b_decode_32l a step is one decode call (the newest
+token of every layer over its 10,000 + 228 keys; out only), timed the same way.
+
 Prints one JSON line. The roofline object is for the attention kernel alone,
 timed with HIP events recorded on its stream around every launch.
 """
@@ -30,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KV tokens/s through attention+impact+top-k; % of HBM / MFMA roofline"
+METRIC_DECODE = "KV tokens/s through one decode step; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -42,15 +46,16 @@ def log(*a):
 def algorithmic_work(wl):
     """Bytes and FLOPs a perfect kernel must move / do for one launch:
     K and V of every key once (2 * H_kv * d * s per key), Q and out once
-    (2 * H * d * s per row), the impact vector once (4 B per key); FLOPs
-    4 * H * d per visible (row, key) pair (Q.K^T and P.V)."""
+    (2 * H * d * s per row), the impact vector once (4 B per key; not in a
+    decode step); FLOPs 4 * H * d per visible (row, key) pair (Q.K^T and P.V)."""
     s = 2 if wl.dtype == "bf16" else 4
+    decode = bool(wl.spec and wl.spec.decode)
     nbytes = 0
     pairs = 0
     for p in wl.problems:
         N = p.n_keys
         rows = p.q_len if wl.mode == "query" else N
-        nbytes += N * 2 * wl.H_kv * wl.d * s + rows * 2 * wl.H * wl.d * s + N * 4
+        nbytes += N * 2 * wl.H_kv * wl.d * s + rows * 2 * wl.H * wl.d * s + (0 if decode else N * 4)
         if wl.mode == "query":   # the q_len rows are the last positions
             pairs += p.q_len * (N - p.q_len) + p.q_len * (p.q_len + 1) // 2
         else:
@@ -185,12 +190,20 @@ def main():
     imps = [pr["impact"] for pr in problems]
     torch.cuda.synchronize()
 
-    plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    if wl.spec.decode:
+        plan = {"kernel": "decode_split+merge", "row_tiles": 1, "workgroups": None}
+    else:
+        plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
     log("plan: %s" % plan)
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
 
+    decode = bool(wl.spec.decode)
+
     def step(events=None):
+        if decode:   # one decode step: out only
+            crkv.crkv_decode_chunks_batched(problems, wl.H, wl.H_kv, wl.d, timing_events=events)
+            return
         crkv.crkv_attn_chunks_batched(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode,
                                       timing_events=events)
         crkv.crkv_topk_batched(imps, ns, ks, idx)
@@ -221,7 +234,8 @@ def main():
     traffic = measured_traffic(args.config)
     hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-           "kernel": "attn_%s_kernel" % plan["kernel"], "row_tiles": plan["row_tiles"],
+           "kernel": plan["kernel"] if decode else "attn_%s_kernel" % plan["kernel"],
+           "row_tiles": plan["row_tiles"],
            "workgroups": plan["workgroups"],
            "kernel_ms": round(k_ms, 4), "alg_bytes_per_launch": nbytes}
     mfma = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
@@ -239,7 +253,11 @@ def main():
     else:
         cfg.update({"chunks": spec.ragged_m, "chunk_len": list(spec.ragged_chunk),
                     "q_len": list(spec.ragged_q)})
-    rec = {"metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
+    if spec.gen_len:
+        cfg["gen_len"] = spec.gen_len
+    if decode:
+        cfg["step"] = "decode"
+    rec = {"metric": METRIC_DECODE if decode else METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic", "config": cfg, "roofline": primary, "roofline_other": secondary,

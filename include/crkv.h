@@ -154,6 +154,29 @@ int64_t crkv_budget(int64_t n_doc, double r);
 size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                            const crkv_opts *opts);
 
+/*
+ * One decode step over the segment table, for a batch of problems (TurboRAG
+ * summary: the generation loop appends each generated token's K/V to the
+ * cache and the newest token attends to every cached key). Each problem has
+ * q_len == 1; chunk_len[m] >= 1 counts the tokens generated so far including
+ * the current one, whose query row (the last position) sees every key.
+ * Computes out only: the problems' impact pointers are ignored (may be NULL).
+ *  Q    device, [H][1][d]; out device, [H][1][d], written
+ *  Requires opts->dtype == CRKV_BF16 (else CRKV_E_UNSUPPORTED) and
+ *  H / H_kv <= 16. opts->mode is ignored. The keys of each (problem, KV head)
+ *  are split into ranges processed in parallel and merged in range order, so
+ *  results are deterministic. Scratch: opts->workspace of at least
+ *  crkv_decode_workspace_size bytes, or library-managed (stream-ordered).
+ *  opts->timing_events bracket the two decode kernels.
+ */
+int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                               const crkv_opts *opts);
+
+/* Bytes of device scratch crkv_decode_chunks_batched needs for these
+ * arguments (256-byte aligned workspace). Returns 0 if they are invalid. */
+size_t crkv_decode_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                                  const crkv_opts *opts);
+
 /* The launch configuration crkv_attn_chunks_batched would use for these
  * arguments: *kernel = 0 for the fp32 kernel, 1 for the bf16 kernel with one
  * wave per SIMD, 2 for the bf16 kernel with producer/consumer wave pairs;

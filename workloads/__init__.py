@@ -64,6 +64,8 @@ class ConfigSpec:
     ragged_q: tuple = (0, 0)        # inclusive bounds of q_len
     k_outliers: int = 0             # outlier channels per KV head in K
     outlier_scale: float = 8.0
+    gen_len: int = 0                # earlier generated tokens in the query block's segment
+    decode: bool = False            # a decode step (out only, no impact or selection)
     description: str = ""
 
     @property
@@ -101,8 +103,17 @@ CONFIGS = {
         ragged_q=(32, 256),
         description="ragged batch of 16 requests, 4 chunks U[1024,4096] + q U[32,256]; "
                     "64 query / 8 KV heads, d=128, bf16 (70B-shaped layer)"),
+    # A decode step after the 10,000 + 100 prefill (TurboRAG's generation
+    # loop): 128 tokens generated so far, the current one is the query row.
+    "llama3_8b_decode_32l": ConfigSpec(
+        name="llama3_8b_decode_32l", index=5, n_problems=32, H=32, H_kv=8, d=128,
+        dtype="bf16", mode="query", r=0.15, chunk_lens=(2500,) * 4, q_len=1, gen_len=227,
+        k_outliers=4, decode=True,
+        description="decode step of the Llama-3-8B-shaped GQA workload: 32 layers, 4 chunks x 2500 "
+                    "+ 100 prompt + 127 generated + the current token (q_len = 1)"),
 }
-CONFIG_ORDER = ["tiny", "llama2_7b_layer", "llama3_8b_gqa_32l", "cross_doc", "ragged_70b"]
+CONFIG_ORDER = ["tiny", "llama2_7b_layer", "llama3_8b_gqa_32l", "cross_doc", "ragged_70b",
+                "llama3_8b_decode_32l"]
 
 
 @dataclass
@@ -207,7 +218,8 @@ def generate(name: str, problems: Optional[Sequence[int]] = None,
     for p in ids:
         rng = np.random.default_rng(np.random.SeedSequence(spec.seed, spawn_key=(p,)))
         wl.problems.append(make_problem(rng, doc_lens[p], q_lens[p], spec.H, spec.H_kv, spec.d,
-                                        spec.dtype, spec.mode, ko, spec.outlier_scale))
+                                        spec.dtype, spec.mode, ko, spec.outlier_scale,
+                                        gen_len=spec.gen_len))
         wl.problem_ids.append(p)
     return wl
 
