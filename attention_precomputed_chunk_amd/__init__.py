@@ -182,19 +182,39 @@ def crkv_attn_chunks(Q, chunk_K: Sequence, chunk_V: Sequence, chunk_len: Sequenc
 
 
 def _problems(problems):
+    if isinstance(problems, Batch):
+        return problems.keep, problems.arr
     ps = [_Problem(pr["Q"], pr["chunk_K"], pr["chunk_V"], pr["chunk_len"], pr["q_len"], pr["out"],
                    pr.get("impact")) for pr in problems]
     arr = (crkv_problem * len(ps))(*[p.c for p in ps])
     return ps, arr
 
 
+class Batch:
+    """Problems marshalled once into their C structures, for repeated calls on
+    the same tensors (a decode loop, a benchmark): every batched function takes
+    a Batch in place of the list of dicts."""
+
+    def __init__(self, problems: Sequence[dict]):
+        self.keep, self.arr = _problems(problems)
+        self.dtype = _dtype_code(problems[0]["Q"])
+
+    def __len__(self):
+        return len(self.keep)
+
+
+def _batch_dtype(problems):
+    return problems.dtype if isinstance(problems, Batch) else _dtype_code(problems[0]["Q"])
+
+
 def crkv_attn_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int,
                              mode: str = "query", stream=None, workspace=None,
                              workspace_bytes: int = 0, timing_events=None,
                              dtype: Optional[int] = None):
-    """problems: dicts with keys Q, chunk_K, chunk_V, chunk_len, q_len, out, impact."""
+    """problems: dicts with keys Q, chunk_K, chunk_V, chunk_len, q_len, out, impact
+    (or a Batch of them)."""
     keep, arr = _problems(problems)
-    o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream,
+    o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream,
                   workspace, workspace_bytes, timing_events)
     _check(lib().crkv_attn_chunks_batched(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
 
@@ -202,7 +222,7 @@ def crkv_attn_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int
 def crkv_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: str = "query",
                         dtype: Optional[int] = None) -> int:
     keep, arr = _problems(problems)
-    o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream=0)
+    o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream=0)
     return int(lib().crkv_workspace_size(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
 
 
@@ -228,7 +248,7 @@ def crkv_plan_info(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: st
                    dtype: Optional[int] = None) -> dict:
     """Launch configuration the planner picks: kernel name, row tiles, workgroups."""
     keep, arr = _problems(problems)
-    o = make_opts(_dtype_code(problems[0]["Q"]) if dtype is None else dtype, mode, stream=0)
+    o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream=0)
     k, rt, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(lib().crkv_plan_info(arr, len(keep), H, H_kv, d, ctypes.byref(o), ctypes.byref(k),
                                 ctypes.byref(rt), ctypes.byref(wg)))

@@ -1,10 +1,12 @@
 // Host side of the crkv C ABI: argument validation, the per-call plan
 // (segment table, key tiles, work items, impact-partial slots), the upload of
-// that plan through a pinned staging ring, and the kernel launches.
+// that plan through a per-device ring on a copy stream, and the kernel
+// launches.
 //
 // Nothing here synchronises the caller's stream. The only host waits are on
-// staging-ring events, which complete once an earlier call's table upload
-// has been consumed.
+// ring-slot events, which complete once the work of the call four uploads
+// earlier has run, and, when the library's scratch buffer or a ring slot has
+// to grow, on the work of the call that used it last.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -31,6 +33,7 @@ hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
 hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
 hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream);
+hipError_t launch_topk_inline(const TopkDesc *descs, int n, hipStream_t stream);
 }  // namespace crkv
 
 using namespace crkv;
@@ -60,83 +63,179 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// ------------------------------------------------------------ pinned staging ring
-// Plan tables are written into pinned host memory and copied to the device
-// on the caller's stream. A slot is reused only after the event recorded
-// behind its copy has completed.
-struct StagingRing {
-    static constexpr int kSlots = 8;
+// ------------------------------------------------------------ plan upload ring
+// A call's plan tables are written into the pinned host half of a ring slot
+// and copied to the slot's device half on a copy stream the library owns per
+// device; the caller's stream waits for that copy on an event. The copy
+// therefore runs while earlier work on the caller's stream still executes
+// (an upload on the caller's stream itself was measured to leave a gap of
+// tens of microseconds between kernels: the hand-off to the copy engine and
+// back). A slot is reused only after the event recorded behind the work that
+// read it has completed, so a slot in use is never overwritten. The ring's
+// mutex is held from plan_acquire to plan_release.
+struct PlanRing {
+    static constexpr int kSlots = 4;
     struct Slot {
-        void *host = nullptr;
+        unsigned char *host = nullptr;
+        unsigned char *dev = nullptr;
         size_t cap = 0;
-        hipEvent_t ev = nullptr;
+        hipEvent_t copied = nullptr;
+        hipEvent_t consumed = nullptr;
         bool pending = false;
     };
     std::mutex mu;
+    hipStream_t copy = nullptr;
     Slot slots[kSlots];
     int next = 0;
 };
 
 std::mutex g_rings_mu;
-std::map<int, std::unique_ptr<StagingRing>> g_rings;
+std::map<int, std::unique_ptr<PlanRing>> g_rings;
 
-StagingRing *ring_for_device(int dev)
-{
-    std::lock_guard<std::mutex> lk(g_rings_mu);
-    auto &r = g_rings[dev];
-    if (!r)
-        r.reset(new StagingRing());
-    return r.get();
-}
+struct PlanLease {
+    PlanRing *ring = nullptr;
+    PlanRing::Slot *slot = nullptr;
+    unsigned char *host = nullptr;   // write the tables here
+    unsigned char *dev = nullptr;    // their device address
+    bool committed = false;
+};
 
-// Copies `bytes` from `src` to device `dst` on `stream` through the ring.
-int staged_upload(void *dst, const void *src, size_t bytes, hipStream_t stream)
+// Takes the next ring slot with room for `bytes` of tables.
+int plan_acquire(PlanLease &l, size_t bytes)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e, "hipGetDevice");
-    StagingRing *ring = ring_for_device(dev);
-    std::lock_guard<std::mutex> lk(ring->mu);
-    StagingRing::Slot &s = ring->slots[ring->next];
-    ring->next = (ring->next + 1) % StagingRing::kSlots;
-    if (s.pending) {
-        e = hipEventSynchronize(s.ev);
-        if (e != hipSuccess)
-            return hip_fail(e, "hipEventSynchronize(staging)");
-        s.pending = false;
+    PlanRing *ring;
+    {
+        std::lock_guard<std::mutex> lk(g_rings_mu);
+        auto &r = g_rings[dev];
+        if (!r)
+            r.reset(new PlanRing());
+        ring = r.get();
     }
-    if (!s.ev) {
-        e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    ring->mu.lock();
+    auto bail = [&](hipError_t err, const char *what) {
+        ring->mu.unlock();
+        return hip_fail(err, what);
+    };
+    if (!ring->copy) {
+        e = hipStreamCreateWithFlags(&ring->copy, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            ring->copy = nullptr;
+            return bail(e, "hipStreamCreate(plan copy)");
+        }
+    }
+    PlanRing::Slot &s = ring->slots[ring->next];
+    if (!s.copied) {
+        e = hipEventCreateWithFlags(&s.copied, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            s.copied = nullptr;
+            return bail(e, "hipEventCreate(plan)");
+        }
+    }
+    if (!s.consumed) {
+        e = hipEventCreateWithFlags(&s.consumed, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            s.consumed = nullptr;
+            return bail(e, "hipEventCreate(plan)");
+        }
+    }
+    if (s.pending) {
+        e = hipEventSynchronize(s.consumed);
         if (e != hipSuccess)
-            return hip_fail(e, "hipEventCreate(staging)");
+            return bail(e, "hipEventSynchronize(plan slot)");
+        s.pending = false;
     }
     if (s.cap < bytes) {
         if (s.host)
             (void)hipHostFree(s.host);
+        if (s.dev)
+            (void)hipFree(s.dev);
         s.host = nullptr;
+        s.dev = nullptr;
         s.cap = 0;
-        const size_t cap = std::max<size_t>(align_up(bytes, 65536), 65536);
-        e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
-        if (e != hipSuccess)
-            return hip_fail(e, "hipHostMalloc(staging)");
+        const size_t cap = align_up(std::max<size_t>(bytes, 65536), 65536);
+        e = hipHostMalloc(reinterpret_cast<void **>(&s.host), cap, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            s.host = nullptr;
+            return bail(e, "hipHostMalloc(plan)");
+        }
+        e = hipMalloc(reinterpret_cast<void **>(&s.dev), cap);
+        if (e != hipSuccess) {
+            s.dev = nullptr;
+            return bail(e, "hipMalloc(plan)");
+        }
         s.cap = cap;
     }
-    memcpy(s.host, src, bytes);
-    e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync(plan)");
-    e = hipEventRecord(s.ev, stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "hipEventRecord(staging)");
-    s.pending = true;
+    ring->next = (ring->next + 1) % PlanRing::kSlots;
+    l.ring = ring;
+    l.slot = &s;
+    l.host = s.host;
+    l.dev = s.dev;
+    l.committed = false;
     return CRKV_OK;
 }
 
+// Enqueues the copy of the slot's first `bytes` and makes `stream` wait for it.
+int plan_commit(PlanLease &l, size_t bytes, hipStream_t stream)
+{
+    PlanRing::Slot &s = *l.slot;
+    hipError_t e = hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, l.ring->copy);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(plan)");
+    e = hipEventRecord(s.copied, l.ring->copy);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(stream, s.copied, 0);
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(l.ring->copy);
+        return hip_fail(e, "plan copy ordering");
+    }
+    l.committed = true;
+    return CRKV_OK;
+}
+
+// Marks the slot busy until the work enqueued on `stream` so far has run.
+void plan_release(PlanLease &l, hipStream_t stream)
+{
+    if (!l.ring)
+        return;
+    PlanRing::Slot &s = *l.slot;
+    if (l.committed) {
+        if (hipEventRecord(s.consumed, stream) == hipSuccess)
+            s.pending = true;
+        else
+            (void)hipStreamSynchronize(stream);
+    }
+    l.ring->mu.unlock();
+    l.ring = nullptr;
+    l.slot = nullptr;
+}
+
 // ------------------------------------------------------------ scratch
+// Without a caller workspace, a call uses one scratch buffer the library keeps
+// per device (a per-call stream-ordered free was measured to block the host
+// until the launched kernels finished, which serialises host preparation with
+// the GPU). The buffer grows when a call needs more and lives until the
+// process ends. Calls that share it are ordered on the device: a call on a
+// different stream from the previous user waits on the event recorded behind
+// that user's work. The mutex is held from scratch_get to scratch_release.
+struct ScratchCache {
+    std::mutex mu;
+    void *ptr = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    hipStream_t last = nullptr;
+    bool used = false;
+};
+
+std::mutex g_scratch_mu;
+std::map<int, std::unique_ptr<ScratchCache>> g_scratch;
+
 struct Scratch {
     void *ptr = nullptr;
-    bool owned = false;
+    ScratchCache *cache = nullptr;   // non-null while the library buffer is held
 };
 
 int scratch_get(Scratch &sc, size_t bytes, const crkv_opts &o, hipStream_t stream)
@@ -148,22 +247,81 @@ int scratch_get(Scratch &sc, size_t bytes, const crkv_opts &o, hipStream_t strea
         if (reinterpret_cast<uintptr_t>(o.workspace) & 255u)
             return fail(CRKV_E_INVAL, "workspace must be 256-byte aligned");
         sc.ptr = o.workspace;
-        sc.owned = false;
+        sc.cache = nullptr;
         return CRKV_OK;
     }
-    hipError_t e = hipMallocAsync(&sc.ptr, std::max<size_t>(bytes, 256), stream);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
-        return hip_fail(e, "hipMallocAsync(scratch)");
-    sc.owned = true;
+        return hip_fail(e, "hipGetDevice");
+    ScratchCache *c;
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        auto &p = g_scratch[dev];
+        if (!p)
+            p.reset(new ScratchCache());
+        c = p.get();
+    }
+    c->mu.lock();
+    if (!c->ev) {
+        e = hipEventCreateWithFlags(&c->ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            c->ev = nullptr;
+            c->mu.unlock();
+            return hip_fail(e, "hipEventCreate(scratch)");
+        }
+    }
+    if (c->used && c->last != stream) {
+        e = hipStreamWaitEvent(stream, c->ev, 0);
+        if (e != hipSuccess) {
+            c->mu.unlock();
+            return hip_fail(e, "hipStreamWaitEvent(scratch)");
+        }
+    }
+    if (c->cap < bytes) {
+        if (c->ptr) {
+            // the previous user's work must be done before the memory goes
+            e = hipEventSynchronize(c->ev);
+            if (e == hipSuccess)
+                e = hipFree(c->ptr);
+            c->ptr = nullptr;
+            c->cap = 0;
+            if (e != hipSuccess) {
+                c->mu.unlock();
+                return hip_fail(e, "hipFree(scratch)");
+            }
+        }
+        const size_t cap = align_up(std::max<size_t>(bytes, 1), size_t(1) << 20);
+        e = hipMalloc(&c->ptr, cap);
+        if (e != hipSuccess) {
+            c->ptr = nullptr;
+            c->mu.unlock();
+            return hip_fail(e, "hipMalloc(scratch)");
+        }
+        c->cap = cap;
+    }
+    sc.ptr = c->ptr;
+    sc.cache = c;
     return CRKV_OK;
 }
 
+// Ends the call's use of the scratch: records the library buffer's event
+// behind the work just enqueued on `stream` and lets the next call have it.
 void scratch_release(Scratch &sc, hipStream_t stream)
 {
-    if (sc.owned && sc.ptr)
-        (void)hipFreeAsync(sc.ptr, stream);
+    if (ScratchCache *c = sc.cache) {
+        if (hipEventRecord(c->ev, stream) == hipSuccess) {
+            c->last = stream;
+            c->used = true;
+        } else {
+            // nothing to order against: make the next user wait for the device
+            (void)hipDeviceSynchronize();
+            c->used = false;
+        }
+        c->mu.unlock();
+    }
     sc.ptr = nullptr;
-    sc.owned = false;
+    sc.cache = nullptr;
 }
 
 // ------------------------------------------------------------ validation
@@ -236,7 +394,8 @@ struct Plan {
     std::vector<ItemDesc> items;
     std::vector<size_t> seg_base, tile_base, slot_base, partial_base;   // per problem
     size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0;
-    size_t table_bytes = 0, off_partial = 0, total_bytes = 0;
+    size_t table_bytes = 0;     // plan tables (uploaded through the ring)
+    size_t scratch_bytes = 0;   // impact partials (workspace or library scratch)
     int max_keys = 0;
     int rt = 1;                 // row tiles per wave (wave kernel) or wave pair (pair kernel)
     int kernel = kBf16Wave;     // bf16 kernel of the launch
@@ -426,19 +585,20 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
     pl.off_tiles = align_up(pl.off_segs + pl.segs.size() * sizeof(SegDesc), 256);
     pl.off_slots = align_up(pl.off_tiles + pl.tiles.size() * sizeof(KTile), 256);
     pl.table_bytes = align_up(pl.off_slots + pl.slot_end.size() * sizeof(int32_t), 256);
-    pl.off_partial = pl.table_bytes;
-    pl.total_bytes = pl.off_partial + partial_floats * sizeof(float);
+    pl.scratch_bytes = std::max<size_t>(partial_floats * sizeof(float), 256);
 }
 
-// Writes the plan tables (with device addresses inside `dev`) into `host`.
-void fill_tables(Plan &pl, const crkv_problem *problems, unsigned char *host, unsigned char *dev)
+// Writes the plan tables (with device addresses inside `dev`, the tables'
+// device copy, and `scratch`, the partials) into `host`.
+void fill_tables(Plan &pl, const crkv_problem *problems, unsigned char *host, unsigned char *dev,
+                 float *scratch)
 {
     for (size_t pi = 0; pi < pl.probs.size(); ++pi) {
         ProbDesc &pd = pl.probs[pi];
         pd.Q = problems[pi].Q;
         pd.out = problems[pi].out;
         pd.impact = problems[pi].impact;
-        pd.partial = reinterpret_cast<float *>(dev + pl.off_partial) + pl.partial_base[pi];
+        pd.partial = scratch + pl.partial_base[pi];
         pd.tiles = reinterpret_cast<const KTile *>(dev + pl.off_tiles) + pl.tile_base[pi];
         pd.segs = reinterpret_cast<const SegDesc *>(dev + pl.off_segs) + pl.seg_base[pi];
         pd.slot_end = reinterpret_cast<const int32_t *>(dev + pl.off_slots) + pl.slot_base[pi];
@@ -499,8 +659,11 @@ int check_topk_args(const float *impact, int n, int k, const int32_t *idx, int w
 // ================================================================== C ABI
 
 // ------------------------------------------------------------ decode plan
-// Workgroups the split of a decode launch aims for (8 per CU of MI355X).
-constexpr int64_t kDecodeTargetItems = 8 * 256;
+// Workgroups the split of a decode launch aims for: two per CU of MI355X
+// (the split kernel's occupancy), i.e. one round; measured best among
+// 256 .. 8192 on the 32-layer decode workload (more rounds add merge work and
+// a partial last round).
+constexpr int64_t kDecodeTargetItems = 2 * 256;
 
 struct DecodePlan {
     std::vector<ProbDesc> probs;
@@ -509,7 +672,8 @@ struct DecodePlan {
     std::vector<DecodePair> pairs;
     std::vector<size_t> tile_base;   // per problem
     size_t off_probs = 0, off_items = 0, off_pairs = 0, off_tiles = 0;
-    size_t table_bytes = 0, off_part = 0, total_bytes = 0;
+    size_t table_bytes = 0;     // plan tables (uploaded through the ring)
+    size_t scratch_bytes = 0;   // per-range partials (workspace or library scratch)
     int split = 0;   // key tiles per range
 };
 
@@ -610,8 +774,7 @@ void build_decode_plan(DecodePlan &pl, const crkv_problem *problems, int n_probl
     pl.off_pairs = align_up(pl.off_items + pl.items.size() * sizeof(DecodeItem), 256);
     pl.off_tiles = align_up(pl.off_pairs + pl.pairs.size() * sizeof(DecodePair), 256);
     pl.table_bytes = align_up(pl.off_tiles + pl.tiles.size() * sizeof(KTile), 256);
-    pl.off_part = pl.table_bytes;
-    pl.total_bytes = pl.off_part + pl.items.size() * (size_t)G * (2 + d) * sizeof(float);
+    pl.scratch_bytes = std::max<size_t>(pl.items.size() * (size_t)G * (2 + d) * sizeof(float), 256);
     (void)H;
 }
 
@@ -638,7 +801,7 @@ size_t crkv_decode_workspace_size(const crkv_problem *problems, int n_problems, 
         return 0;
     DecodePlan pl;
     build_decode_plan(pl, problems, n_problems, H, H_kv, d);
-    return pl.total_bytes;
+    return pl.scratch_bytes;
 }
 
 int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
@@ -652,23 +815,31 @@ int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int
     DecodePlan pl;
     build_decode_plan(pl, problems, n_problems, H, H_kv, d);
     Scratch sc;
-    rc = scratch_get(sc, pl.total_bytes, o, stream);
+    rc = scratch_get(sc, pl.scratch_bytes, o, stream);
     if (rc)
         return rc;
-    unsigned char *dev = static_cast<unsigned char *>(sc.ptr);
+    PlanLease lease;
+    rc = plan_acquire(lease, pl.table_bytes);
+    if (rc) {
+        scratch_release(sc, stream);
+        return rc;
+    }
+    unsigned char *dev = lease.dev;
     for (int pi = 0; pi < n_problems; ++pi) {
         ProbDesc &pd = pl.probs[pi];
         pd.Q = problems[pi].Q;
         pd.out = problems[pi].out;
         pd.tiles = reinterpret_cast<const KTile *>(dev + pl.off_tiles) + pl.tile_base[pi];
     }
-    std::vector<unsigned char> host(pl.table_bytes, 0);
-    memcpy(host.data() + pl.off_probs, pl.probs.data(), pl.probs.size() * sizeof(ProbDesc));
-    memcpy(host.data() + pl.off_items, pl.items.data(), pl.items.size() * sizeof(DecodeItem));
-    memcpy(host.data() + pl.off_pairs, pl.pairs.data(), pl.pairs.size() * sizeof(DecodePair));
-    memcpy(host.data() + pl.off_tiles, pl.tiles.data(), pl.tiles.size() * sizeof(KTile));
-    rc = staged_upload(dev, host.data(), pl.table_bytes, stream);
+    unsigned char *host = lease.host;
+    memset(host, 0, pl.table_bytes);
+    memcpy(host + pl.off_probs, pl.probs.data(), pl.probs.size() * sizeof(ProbDesc));
+    memcpy(host + pl.off_items, pl.items.data(), pl.items.size() * sizeof(DecodeItem));
+    memcpy(host + pl.off_pairs, pl.pairs.data(), pl.pairs.size() * sizeof(DecodePair));
+    memcpy(host + pl.off_tiles, pl.tiles.data(), pl.tiles.size() * sizeof(KTile));
+    rc = plan_commit(lease, pl.table_bytes, stream);
     if (rc) {
+        plan_release(lease, stream);
         scratch_release(sc, stream);
         return rc;
     }
@@ -676,7 +847,7 @@ int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int
     args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
     args.items = reinterpret_cast<const DecodeItem *>(dev + pl.off_items);
     args.pairs = reinterpret_cast<const DecodePair *>(dev + pl.off_pairs);
-    args.part = reinterpret_cast<float *>(dev + pl.off_part);
+    args.part = static_cast<float *>(sc.ptr);
     args.G = H / H_kv;
     args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     hipError_t e = hipSuccess;
@@ -686,6 +857,7 @@ int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int
         e = launch_decode_bf16(d, args, (int)pl.items.size(), (int)pl.pairs.size(), stream);
     if (e == hipSuccess && o.timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    plan_release(lease, stream);
     scratch_release(sc, stream);
     if (e != hipSuccess)
         return hip_fail(e, "decode launch");
@@ -721,7 +893,7 @@ size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, 
         return 0;
     Plan pl;
     build_plan(pl, problems, n_problems, H, H_kv, d, o);
-    return pl.total_bytes;
+    return pl.scratch_bytes;
 }
 
 int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
@@ -753,14 +925,20 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
     build_plan(pl, problems, n_problems, H, H_kv, d, o);
 
     Scratch sc;
-    rc = scratch_get(sc, pl.total_bytes, o, stream);
+    rc = scratch_get(sc, pl.scratch_bytes, o, stream);
     if (rc)
         return rc;
-    unsigned char *dev = static_cast<unsigned char *>(sc.ptr);
-    std::vector<unsigned char> host(pl.table_bytes);
-    fill_tables(pl, problems, host.data(), dev);
-    rc = staged_upload(dev, host.data(), pl.table_bytes, stream);
+    PlanLease lease;
+    rc = plan_acquire(lease, pl.table_bytes);
     if (rc) {
+        scratch_release(sc, stream);
+        return rc;
+    }
+    unsigned char *dev = lease.dev;
+    fill_tables(pl, problems, lease.host, dev, static_cast<float *>(sc.ptr));
+    rc = plan_commit(lease, pl.table_bytes, stream);
+    if (rc) {
+        plan_release(lease, stream);
         scratch_release(sc, stream);
         return rc;
     }
@@ -784,6 +962,7 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
     if (e == hipSuccess)
         e = launch_combine(args.probs, n_problems, pl.max_keys, stream);
+    plan_release(lease, stream);
     scratch_release(sc, stream);
     if (e != hipSuccess)
         return hip_fail(e, "attention launch");
@@ -841,20 +1020,23 @@ int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_
         hipError_t e = launch_topk_one(descs[0], stream);
         return e == hipSuccess ? CRKV_OK : hip_fail(e, "top-k launch");
     }
-    const size_t bytes = align_up(descs.size() * sizeof(TopkDesc), 256);
-    Scratch sc;
-    int rc = scratch_get(sc, bytes, o, stream);
+    if (n_problems <= kTopkInline) {   // descriptors travel as kernel arguments
+        hipError_t e = launch_topk_inline(descs.data(), n_problems, stream);
+        return e == hipSuccess ? CRKV_OK : hip_fail(e, "top-k launch");
+    }
+    const size_t bytes = descs.size() * sizeof(TopkDesc);
+    PlanLease lease;
+    int rc = plan_acquire(lease, bytes);
     if (rc)
         return rc;
-    std::vector<unsigned char> host(bytes, 0);
-    memcpy(host.data(), descs.data(), descs.size() * sizeof(TopkDesc));
-    rc = staged_upload(sc.ptr, host.data(), bytes, stream);
-    if (rc) {
-        scratch_release(sc, stream);
+    memcpy(lease.host, descs.data(), bytes);
+    rc = plan_commit(lease, bytes, stream);
+    hipError_t e = hipSuccess;
+    if (rc == CRKV_OK)
+        e = launch_topk_batched(reinterpret_cast<const TopkDesc *>(lease.dev), n_problems, stream);
+    plan_release(lease, stream);
+    if (rc)
         return rc;
-    }
-    hipError_t e = launch_topk_batched(static_cast<const TopkDesc *>(sc.ptr), n_problems, stream);
-    scratch_release(sc, stream);
     return e == hipSuccess ? CRKV_OK : hip_fail(e, "top-k launch");
 }
 

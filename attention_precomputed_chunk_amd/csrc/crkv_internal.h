@@ -123,4 +123,11 @@ struct TopkDesc {
     int32_t n, k;
 };
 
+// Batches of up to kTopkInline top-k problems pass their descriptors as
+// kernel arguments (no table upload).
+constexpr int kTopkInline = 64;
+struct TopkInline {
+    TopkDesc d[kTopkInline];
+};
+
 }  // namespace crkv

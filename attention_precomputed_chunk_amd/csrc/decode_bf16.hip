@@ -22,8 +22,10 @@
 // LDS and written as one partial: per head (max, sum) and the output row
 // scaled to that max.
 //
-// Merge kernel: for each (problem, KV head), the partials of its ranges are
-// combined in range order (deterministic) and out = O / sum is written in bf16.
+// Merge kernel: for each (problem, KV head), the heads' overall max and sum
+// come from the partials' (max, sum); each partial's weight per head is
+// staged in LDS, and every output element sums its partials in range order
+// (deterministic) and is written in bf16.
 #include "attn_bf16_common.h"
 
 namespace crkv {
@@ -210,30 +212,65 @@ __global__ void __launch_bounds__(kDecodeThreads, 2) decode_split_kernel(const D
     }
 }
 
+// Partials a merge workgroup stages in LDS at once (more are merged in chunks).
+constexpr int kMergeChunk = 64;
+
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeArgs a)
 {
+    __shared__ float w_lds[kMergeChunk][kDecodeMaxGroup];   // weight of partial p for head r
+    __shared__ float s_max[kDecodeMaxGroup], s_sum[kDecodeMaxGroup];
     const DecodePair pp = a.pairs[blockIdx.x];
     const ProbDesc pr = a.probs[pp.prob];
     const int G = a.G;
     const float c = a.c_log2;
     const size_t stride = (size_t)G * (2 + D);
     const float *base = a.part + (size_t)pp.part_begin * stride;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int r = idx / D, dd = idx % D;
+    const int tid = threadIdx.x;
+    // the overall max and sum of each head, from the partials' (max, sum)
+    if (tid < G) {
         float M = -INFINITY;
         for (int p = 0; p < pp.n_parts; ++p)
-            M = fmaxf(M, base[p * stride + 2 * r]);
-        float L = 0.f, O = 0.f;
-        for (int p = 0; p < pp.n_parts; ++p) {
-            const float *q = base + p * stride;
-            const float f = exp2_hw((q[2 * r] - M) * c);
-            L = __builtin_fmaf(q[2 * r + 1], f, L);
-            O = __builtin_fmaf(q[2 * G + r * D + dd], f, O);
+            M = fmaxf(M, base[p * stride + 2 * tid]);
+        float L = 0.f;
+        for (int p = 0; p < pp.n_parts; ++p)
+            L = __builtin_fmaf(base[p * stride + 2 * tid + 1], exp2_hw((base[p * stride + 2 * tid] - M) * c), L);
+        s_max[tid] = M;
+        s_sum[tid] = L;
+    }
+    __syncthreads();
+    float acc[(kDecodeMaxGroup * D + 255) / 256];
+#pragma unroll
+    for (int i = 0; i < (kDecodeMaxGroup * D + 255) / 256; ++i)
+        acc[i] = 0.f;
+    for (int p0 = 0; p0 < pp.n_parts; p0 += kMergeChunk) {
+        const int np = min(kMergeChunk, pp.n_parts - p0);
+        for (int x = tid; x < np * G; x += 256) {
+            const int p = x / G, r = x % G;
+            w_lds[p][r] = exp2_hw((base[(p0 + p) * stride + 2 * r] - s_max[r]) * c) / s_sum[r];
         }
-        const int h = pp.kv_head * G + r;
-        const gptr<__bf16> out = as_global(reinterpret_cast<__bf16 *>(pr.out));
-        out[(size_t)h * D + dd] = (__bf16)(O / L);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < (kDecodeMaxGroup * D + 255) / 256; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < G * D) {
+                const int r = idx / D;
+                float o = acc[i];
+                for (int p = 0; p < np; ++p)
+                    o = __builtin_fmaf(base[(p0 + p) * stride + 2 * G + idx], w_lds[p][r], o);
+                acc[i] = o;
+            }
+        }
+        __syncthreads();
+    }
+    const gptr<__bf16> out = as_global(reinterpret_cast<__bf16 *>(pr.out));
+#pragma unroll
+    for (int i = 0; i < (kDecodeMaxGroup * D + 255) / 256; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < G * D) {
+            const int r = idx / D, dd = idx % D;
+            out[(size_t)(pp.kv_head * G + r) * D + dd] = (__bf16)acc[i];
+        }
     }
 }
 

@@ -216,6 +216,11 @@ __global__ void __launch_bounds__(kTopkThreads) topk_batched_kernel(const TopkDe
     topk_body(descs[blockIdx.x]);
 }
 
+__global__ void __launch_bounds__(kTopkThreads) topk_inline_kernel(const TopkInline t)
+{
+    topk_body(t.d[blockIdx.x]);
+}
+
 hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream)
 {
     hipLaunchKernelGGL(topk_one_kernel, dim3(1), dim3(kTopkThreads), 0, stream, td);
@@ -227,6 +232,17 @@ hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream)
     if (n <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(topk_batched_kernel, dim3(n), dim3(kTopkThreads), 0, stream, descs);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_inline(const TopkDesc *descs, int n, hipStream_t stream)
+{
+    if (n <= 0 || n > kTopkInline)
+        return hipErrorInvalidValue;
+    TopkInline t{};
+    for (int i = 0; i < n; ++i)
+        t.d[i] = descs[i];
+    hipLaunchKernelGGL(topk_inline_kernel, dim3(n), dim3(kTopkThreads), 0, stream, t);
     return hipGetLastError();
 }
 

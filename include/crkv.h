@@ -86,8 +86,12 @@ typedef struct crkv_opts {
     int dtype;              /* crkv_dtype of Q, K, V and out                   */
     int mode;               /* crkv_mode                                        */
     void *stream;           /* hipStream_t, NULL = null stream                  */
-    void *workspace;        /* device scratch, or NULL: the library allocates
-                               and frees it stream-ordered on `stream`          */
+    void *workspace;        /* device scratch, or NULL: the library uses a
+                               buffer it keeps per device (grown on demand,
+                               held until exit); calls on different streams
+                               that share it run one after another on the
+                               device, so pass a workspace per stream for
+                               concurrent calls                                 */
     size_t workspace_bytes; /* size of `workspace`; see crkv_workspace_size     */
     void *timing_events[2]; /* optional hipEvent_t pair recorded on `stream`
                                immediately before and after the attention

@@ -164,3 +164,17 @@ def test_plan_info_rejects_invalid():
     bad = [_fake_problem([64], 16, 6, 128)]
     with pytest.raises(crkv.CrkvError):
         crkv.crkv_plan_info(bad, 6, 4, 128, mode="query", dtype=crkv.CRKV_BF16)   # H % H_kv != 0
+
+
+def test_batch_marshals_once_and_plans_the_same(monkeypatch):
+    monkeypatch.delenv("CRKV_BF16_KERNEL", raising=False)
+    monkeypatch.delenv("CRKV_ROW_TILES", raising=False)
+    probs = [_fake_problem([700, 300], 40, 8, 128) for _ in range(3)]
+    b = crkv.Batch.__new__(crkv.Batch)   # fake tensors carry no dtype: set it by hand
+    b.keep, b.arr = crkv._problems(probs)
+    b.dtype = crkv.CRKV_BF16
+    assert len(b) == 3
+    assert (crkv.crkv_plan_info(b, 8, 2, 128, mode="query", dtype=crkv.CRKV_BF16)
+            == crkv.crkv_plan_info(probs, 8, 2, 128, mode="query", dtype=crkv.CRKV_BF16))
+    assert (crkv.crkv_workspace_size(b, 8, 2, 128, dtype=crkv.CRKV_BF16)
+            == crkv.crkv_workspace_size(probs, 8, 2, 128, dtype=crkv.CRKV_BF16))

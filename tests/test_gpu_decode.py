@@ -136,3 +136,41 @@ def test_decode_rejects_bad_arguments():
     dw = DeviceWorkload(wl)
     with pytest.raises(crkv.CrkvError):
         decode(dw)                                   # 17 query heads per KV head
+
+
+def test_library_scratch_across_streams_and_growth():
+    """Without a workspace, calls share the library's per-device scratch:
+    calls on two streams back to back, and calls that need it to grow, give
+    the same results as one call at a time on the default stream."""
+    small = DeviceWorkload(workloads.custom(324, [90, 40], 1, 8, 2, 128, dtype="bf16",
+                                            n_problems=2, gen_len=20))
+    big = DeviceWorkload(workloads.custom(325, [3000, 2100, 700], 1, 8, 1, 128, dtype="bf16",
+                                          n_problems=4, gen_len=60))
+    pre = DeviceWorkload(workloads.custom(326, [500, 260], 33, 8, 2, 128, dtype="bf16",
+                                          n_problems=2))
+    decode(small)
+    decode(big)
+    pre.attn()
+    torch.cuda.synchronize()
+    refs = [[p["out"].clone() for p in dw.problems] for dw in (small, big, pre)]
+    ref_imp = [p["impact"].clone() for p in pre.problems]
+    for dw in (small, big, pre):
+        for p in dw.problems:
+            p["out"].zero_()
+    for p in pre.problems:
+        p["impact"].zero_()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            decode(small, stream=s1)
+        with torch.cuda.stream(s2):
+            decode(big, stream=s2)
+        with torch.cuda.stream(s1):
+            pre.attn(stream=s1)
+    torch.cuda.synchronize()
+    for dw, ref in zip((small, big, pre), refs):
+        for a, p in zip(ref, dw.problems):
+            assert torch.equal(a, p["out"])
+    for a, p in zip(ref_imp, pre.problems):
+        assert torch.equal(a, p["impact"])

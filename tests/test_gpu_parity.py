@@ -302,3 +302,19 @@ def test_topk_batched_matches_single():
     torch.cuda.synchronize()
     for v, k, i in zip(vecs, ks, idx):
         np.testing.assert_array_equal(i.cpu().numpy(), oracle.topk(v, k))
+
+
+@pytest.mark.parametrize("count", [2, 64, 65, 150])
+def test_topk_batched_sizes(count):
+    """Batches up to 64 pass their descriptors as kernel arguments, larger
+    ones upload a table: both against the oracle, bit-exact."""
+    rng = np.random.default_rng(40 + count)
+    ns = rng.integers(1, 3000, size=count)
+    vecs = [rng.standard_normal(int(n)).astype(np.float32) for n in ns]
+    ks = [int(rng.integers(1, n + 1)) for n in ns]
+    dv = [torch.from_numpy(v).to(DEV) for v in vecs]
+    idx = [torch.full((k,), -1, dtype=torch.int32, device=DEV) for k in ks]
+    crkv.crkv_topk_batched(dv, [len(v) for v in vecs], ks, idx)
+    torch.cuda.synchronize()
+    for v, k, i in zip(vecs, ks, idx):
+        np.testing.assert_array_equal(i.cpu().numpy(), oracle.topk(v, k))
