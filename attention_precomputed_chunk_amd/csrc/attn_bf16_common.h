@@ -136,6 +136,18 @@ struct Stager {
 };
 
 // S^T of one 16-row tile against the two 16-key subtiles of a key tile.
+// Sweep 1 keeps per (row, lane group) a reference maximum m and
+// l = sum of exp2((s - m) * c) over the keys seen so far, with m <= their
+// maximum. An unmasked key tile is summed against the current m; the exact
+// maximum is taken again (and l rescaled) only when some lane's sum over the
+// tile exceeds 2^32, i.e. a score lies more than about 29 above m in log2
+// units, which includes a row's first tile (m = -inf gives an infinite sum).
+// lse = m * c + log2(l) is the same quantity either way; skipping the
+// per-tile maximum and rescale removes a third of sweep 1's vector work
+// (used by the one-wave kernel, whose sweep 1 is vector-bound; with two
+// waves per SIMD the pair kernel measured no difference).
+constexpr float kLseRescaleBound = 4294967296.0f;   // 2^32
+
 struct Spair {
     f32x4 s0, s1;
 };

@@ -23,8 +23,10 @@ constexpr int kWaveRowTiles[3] = {4, 5, 7};     // rt the wave kernels are built
 constexpr int kWaveMaxRowTilesCross = 5;        // cross-document wave kernels: 7 would spill
 constexpr int kPairRowTiles[3] = {2, 4, 6};     // rt the pair kernels are built for
 // Planner cost model, SIMD cycles per 32-key step of one workgroup: a fixed
-// part and a part per row tile (fitted to measurements on MI355X).
-constexpr int kWaveStepFixed = 1884, kWaveStepPerTile = 778;
+// part and a part per row tile (fitted to measurements on MI355X; the wave
+// kernel's per-tile part scaled by its measured 9 % gain from the pipelined
+// sweep 2 and the reference-maximum sweep 1).
+constexpr int kWaveStepFixed = 1884, kWaveStepPerTile = 684;
 constexpr int kPairStepFixed = 3166, kPairStepPerTile = 402;
 constexpr int kRowTilesF32 = 4;    // row tiles per wave, fp32 kernels
 constexpr int kTopkMaxK = 8192;    // selection buffer held in LDS
