@@ -121,6 +121,39 @@ def test_forced_bf16_builds(case, build, monkeypatch):
     run_and_compare(wl, label="forced-%s%d-small%d" % (kernel, rt, case))
 
 
+def rising_scores_workload(seed, mode):
+    """Scores that climb by about 80 log2 units along the keys: channel 0 of
+    every key grows with its position and channel 0 of every query row is
+    in [1, 1.4], so each row's running maximum is overtaken by far more than
+    the sweep-1 rescale bound many times over, while every p stays a normal
+    float32."""
+    wl = workloads.custom(seed, [700, 400], 48, 8, 2, 128, dtype="bf16", mode=mode, n_problems=1)
+    p = wl.problems[0]
+    n_keys = sum(p.lens)
+    pos = 0
+    for c, n in enumerate(p.lens):
+        k = workloads.widen(p.K[c], "bf16").astype(np.float32)
+        k[:, :, 0] += (520.0 * np.arange(pos, pos + n) / n_keys).astype(np.float32)
+        p.K[c] = workloads.round_bf16(k)
+        pos += n
+    q = workloads.widen(p.Q, "bf16").astype(np.float32)
+    q[..., 0] = 1.0 + 0.1 * np.abs(q[..., 0])
+    p.Q = workloads.round_bf16(q)
+    return wl
+
+
+@pytest.mark.parametrize("build", [None, ("wave", 4), ("wave", 7), ("pair", 6)],
+                         ids=["planner", "wave4", "wave7", "pair6"])
+def test_rising_scores(build, monkeypatch):
+    """Sweep 1's exact-maximum path taken again and again (a row's maximum
+    keeps rising), against the oracle."""
+    if build:
+        monkeypatch.setenv("CRKV_BF16_KERNEL", build[0])
+        monkeypatch.setenv("CRKV_ROW_TILES", str(build[1]))
+    say("rising scores", build)
+    run_and_compare(rising_scores_workload(350, "query"), label="rising-%s" % (build,))
+
+
 def test_tiny_config():
     """1 layer, 4 heads, d=64, fp32; 2 chunks x 64 + 16 query rows; top-12."""
     say("tiny")
