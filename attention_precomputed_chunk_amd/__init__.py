@@ -53,11 +53,19 @@ class crkv_problem(ctypes.Structure):
                 ("q_len", ctypes.c_int), ("out", ctypes.c_void_p), ("impact", ctypes.c_void_p)]
 
 
+class crkv_kv_select(ctypes.Structure):
+    _fields_ = [("chunk_K", ctypes.POINTER(ctypes.c_void_p)), ("chunk_V", ctypes.POINTER(ctypes.c_void_p)),
+                ("chunk_len", ctypes.POINTER(ctypes.c_int32)), ("m", ctypes.c_int),
+                ("idx", ctypes.c_void_p), ("k", ctypes.c_int), ("K_sel", ctypes.c_void_p),
+                ("V_sel", ctypes.c_void_p)]
+
+
 _lib = None
 
 DECLARED = ["crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
             "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
-            "crkv_decode_chunks_batched", "crkv_decode_workspace_size",
+            "crkv_decode_chunks_batched", "crkv_decode_workspace_size", "crkv_gather_kv",
+            "crkv_scatter_kv",
             "crkv_status_string", "crkv_last_error", "crkv_version"]
 
 
@@ -103,6 +111,10 @@ def lib():
         L.crkv_decode_workspace_size.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
                                                  ctypes.POINTER(crkv_opts)]
         L.crkv_decode_workspace_size.restype = ctypes.c_size_t
+        for name in ("crkv_gather_kv", "crkv_scatter_kv"):
+            f = getattr(L, name)
+            f.argtypes = [ctypes.POINTER(crkv_kv_select), c_int, c_int, c_int, ctypes.POINTER(crkv_opts)]
+            f.restype = c_int
         L.crkv_status_string.argtypes = [c_int]
         L.crkv_status_string.restype = ctypes.c_char_p
         L.crkv_last_error.argtypes = []
@@ -269,6 +281,58 @@ def crkv_topk_batched(impacts: Sequence, ns: Sequence[int], ks: Sequence[int], i
     xp = (ctypes.c_void_p * P)(*[_ptr(x) for x in idxs])
     o = make_opts(stream=stream)
     _check(lib().crkv_topk_batched(ip, nn, kk, xp, P, ctypes.byref(o)))
+
+
+class _Select:
+    """Keeps the ctypes arrays of one crkv_kv_select alive."""
+
+    def __init__(self, sel: dict):
+        lens = sel["chunk_len"]
+        m = len(lens) - 1
+        if len(sel["chunk_K"]) != m + 1 or len(sel["chunk_V"]) != m + 1:
+            raise ValueError("chunk_K, chunk_V and chunk_len need m + 1 entries")
+        self.k = (ctypes.c_void_p * (m + 1))(*[_ptr(x) for x in sel["chunk_K"]])
+        self.v = (ctypes.c_void_p * (m + 1))(*[_ptr(x) for x in sel["chunk_V"]])
+        self.lens = (ctypes.c_int32 * (m + 1))(*[int(x) for x in lens])
+        idx = sel["idx"]
+        n_sel = int(sel["k"]) if "k" in sel else (0 if idx is None else int(idx.numel()))
+        self.c = crkv_kv_select(self.k, self.v, self.lens, m, _ptr(idx), n_sel, _ptr(sel["K_sel"]),
+                                _ptr(sel["V_sel"]))
+
+
+def _selections(sels):
+    if isinstance(sels, SelectBatch):
+        return sels.keep, sels.arr
+    keep = [_Select(s) for s in sels]
+    return keep, (crkv_kv_select * len(keep))(*[s.c for s in keep])
+
+
+class SelectBatch:
+    """Selections marshalled once into their C structures, for repeated
+    gather/scatter calls on the same tensors: both functions take a
+    SelectBatch in place of the list of dicts."""
+
+    def __init__(self, sels: Sequence[dict]):
+        self.keep, self.arr = _selections(list(sels))
+
+    def __len__(self):
+        return len(self.keep)
+
+
+def crkv_gather_kv(sels: Sequence[dict], H_kv: int, d: int, dtype: int, stream=None, timing_events=None):
+    """Gather the selected keys' K/V rows into packed buffers. Each dict:
+    chunk_K, chunk_V (m + 1 tensors or None), chunk_len, idx (int32 device
+    tensor), K_sel, V_sel ([H_kv][k][d]); optional k (default idx.numel())."""
+    keep, arr = _selections(sels)
+    o = make_opts(dtype, "query", stream, timing_events=timing_events)
+    _check(lib().crkv_gather_kv(arr, len(keep), H_kv, d, ctypes.byref(o)))
+
+
+def crkv_scatter_kv(sels: Sequence[dict], H_kv: int, d: int, dtype: int, stream=None, timing_events=None):
+    """Write packed K/V rows back to the selected positions of the segments."""
+    keep, arr = _selections(sels)
+    o = make_opts(dtype, "query", stream, timing_events=timing_events)
+    _check(lib().crkv_scatter_kv(arr, len(keep), H_kv, d, ctypes.byref(o)))
 
 
 def crkv_budget(n_doc: int, r: float) -> int:

@@ -34,6 +34,7 @@ hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipS
 hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
 hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream);
 hipError_t launch_topk_inline(const TopkDesc *descs, int n, hipStream_t stream);
+hipError_t launch_kvsel(bool scatter, const SelArgs &args, int n_items, hipStream_t stream);
 }  // namespace crkv
 
 using namespace crkv;
@@ -778,6 +779,118 @@ void build_decode_plan(DecodePlan &pl, const crkv_problem *problems, int n_probl
     (void)H;
 }
 
+// ------------------------------------------------------------ selected-key K/V gather / scatter
+int validate_sel(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts &o)
+{
+    int rc = check_opts(o);
+    if (rc)
+        return rc;
+    if (n < 1 || !sel)
+        return fail(CRKV_E_INVAL, "n = %d selections (need >= 1, non-null array)", n);
+    if (H_kv < 1)
+        return fail(CRKV_E_INVAL, "H_kv = %d < 1", H_kv);
+    if (d != 64 && d != 128)
+        return fail(CRKV_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", d);
+    for (int p = 0; p < n; ++p) {
+        const crkv_kv_select &q = sel[p];
+        if (q.m < 0)
+            return fail(CRKV_E_INVAL, "selection %d: m = %d < 0", p, q.m);
+        if (!q.chunk_K || !q.chunk_V || !q.chunk_len)
+            return fail(CRKV_E_INVAL, "selection %d: chunk_K, chunk_V and chunk_len must be non-null", p);
+        if (q.k < 0)
+            return fail(CRKV_E_INVAL, "selection %d: k = %d < 0", p, q.k);
+        if (q.k > 0 && (!q.idx || !q.K_sel || !q.V_sel))
+            return fail(CRKV_E_INVAL, "selection %d: idx, K_sel and V_sel must be non-null", p);
+        if (q.k > 0 && (!aligned16(q.K_sel) || !aligned16(q.V_sel)))
+            return fail(CRKV_E_INVAL, "selection %d: K_sel and V_sel must be 16-byte aligned", p);
+        int64_t total = 0;
+        for (int c = 0; c <= q.m; ++c) {
+            const int32_t len = q.chunk_len[c];
+            if (len < 0)
+                return fail(CRKV_E_INVAL, "selection %d: chunk_len[%d] = %d < 0", p, c, len);
+            if (len > 0 && (!q.chunk_K[c] || !q.chunk_V[c]))
+                return fail(CRKV_E_INVAL, "selection %d: chunk %d has %d keys but a null K or V", p, c, len);
+            if (len > 0 && (!aligned16(q.chunk_K[c]) || !aligned16(q.chunk_V[c])))
+                return fail(CRKV_E_INVAL, "selection %d: chunk %d K/V must be 16-byte aligned", p, c);
+            total += len;
+        }
+        if (total >= (int64_t(1) << 30))
+            return fail(CRKV_E_UNSUPPORTED, "selection %d: %lld keys (limit 2^30)", p, (long long)total);
+    }
+    return CRKV_OK;
+}
+
+int run_sel(bool scatter, const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = validate_sel(sel, n, H_kv, d, o);
+    if (rc)
+        return rc;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    std::vector<SelProb> probs(n);
+    std::vector<SelSeg> segs;
+    std::vector<SelItem> items;
+    std::vector<size_t> seg_base(n);
+    for (int p = 0; p < n; ++p) {
+        const crkv_kv_select &q = sel[p];
+        seg_base[p] = segs.size();
+        int32_t start = 0;
+        for (int c = 0; c <= q.m; ++c) {
+            SelSeg sg{};
+            sg.K = q.chunk_K[c];
+            sg.V = q.chunk_V[c];
+            sg.start = start;
+            sg.len = q.chunk_len[c];
+            segs.push_back(sg);
+            start += q.chunk_len[c];
+        }
+        SelProb &pr = probs[p];
+        pr = SelProb{};
+        pr.idx = q.idx;
+        pr.K_sel = q.K_sel;
+        pr.V_sel = q.V_sel;
+        pr.n_seg = q.m + 1;
+        pr.k = q.k;
+        for (int j0 = 0; j0 < q.k; j0 += kSelKeysPerItem)
+            items.push_back(SelItem{p, j0});
+    }
+    if (items.empty())
+        return CRKV_OK;
+    const size_t off_probs = 0;
+    const size_t off_segs = align_up(probs.size() * sizeof(SelProb), 256);
+    const size_t off_items = align_up(off_segs + segs.size() * sizeof(SelSeg), 256);
+    const size_t bytes = align_up(off_items + items.size() * sizeof(SelItem), 256);
+    PlanLease lease;
+    rc = plan_acquire(lease, bytes);
+    if (rc)
+        return rc;
+    for (int p = 0; p < n; ++p)
+        probs[p].segs = reinterpret_cast<const SelSeg *>(lease.dev + off_segs) + seg_base[p];
+    memset(lease.host, 0, bytes);
+    memcpy(lease.host + off_probs, probs.data(), probs.size() * sizeof(SelProb));
+    memcpy(lease.host + off_segs, segs.data(), segs.size() * sizeof(SelSeg));
+    memcpy(lease.host + off_items, items.data(), items.size() * sizeof(SelItem));
+    rc = plan_commit(lease, bytes, stream);
+    hipError_t e = hipSuccess;
+    if (rc == CRKV_OK) {
+        SelArgs args{};
+        args.probs = reinterpret_cast<const SelProb *>(lease.dev + off_probs);
+        args.items = reinterpret_cast<const SelItem *>(lease.dev + off_items);
+        args.H_kv = H_kv;
+        args.row_bytes = d * (o.dtype == CRKV_BF16 ? 2 : 4);
+        if (o.timing_events[0])
+            e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
+        if (e == hipSuccess)
+            e = launch_kvsel(scatter, args, (int)items.size(), stream);
+        if (e == hipSuccess && o.timing_events[1])
+            e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    }
+    plan_release(lease, stream);
+    if (rc)
+        return rc;
+    return e == hipSuccess ? CRKV_OK : hip_fail(e, scatter ? "scatter launch" : "gather launch");
+}
+
 extern "C" {
 
 void crkv_opts_init(crkv_opts *opts)
@@ -1038,6 +1151,16 @@ int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_
     if (rc)
         return rc;
     return e == hipSuccess ? CRKV_OK : hip_fail(e, "top-k launch");
+}
+
+int crkv_gather_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts)
+{
+    return run_sel(false, sel, n, H_kv, d, opts);
+}
+
+int crkv_scatter_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts)
+{
+    return run_sel(true, sel, n, H_kv, d, opts);
 }
 
 }  // extern "C"

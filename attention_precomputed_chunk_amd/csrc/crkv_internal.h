@@ -132,4 +132,39 @@ struct TopkInline {
     TopkDesc d[kTopkInline];
 };
 
+// ---------------------------------------------------------------- selected-key K/V gather / scatter
+constexpr int kSelKeysPerItem = 16;   // selected keys per workgroup
+constexpr int kSelThreads = 256;
+
+struct SelSeg {               // one segment of a problem's table
+    const void *K;            // [H_kv][len][d]
+    const void *V;
+    int32_t start;            // position of its first key in the concatenation
+    int32_t len;
+    int32_t pad0, pad1;
+};
+
+struct SelProb {
+    const SelSeg *segs;       // n_seg = m + 1 segments, in key order
+    const int32_t *idx;       // [k] selected positions
+    void *K_sel;              // [H_kv][k][d]
+    void *V_sel;
+    int32_t n_seg;
+    int32_t k;
+    int32_t pad0, pad1;
+};
+
+struct SelItem {              // keys j0 .. j0 + kSelKeysPerItem - 1 of one problem
+    int32_t prob;
+    int32_t j0;
+};
+
+struct SelArgs {
+    const SelProb *probs;
+    const SelItem *items;
+    int32_t H_kv;
+    int32_t row_bytes;        // d * element size: 128, 256 or 512
+};
+static_assert(sizeof(SelSeg) == 32 && sizeof(SelProb) == 48 && sizeof(SelItem) == 8, "table layout");
+
 }  // namespace crkv

@@ -14,6 +14,11 @@ document tokens + 100 query tokens, r = 0.15), the shape of TurboRAG's
 With --config llama3_8b_decode_32l a step is one decode call (the newest
 token of every layer over its 10,000 + 228 keys; out only), timed the same way.
 
+With --config llama3_8b_select_kv_32l a step moves the K/V rows of every
+layer's selected keys (the top-1500 of the default workload's impact, found
+once before timing): one gather launch into packed buffers and one scatter
+launch back into the segments.
+
 Prints one JSON line. The roofline object is for the attention kernel alone,
 timed with HIP events recorded on its stream around every launch.
 """
@@ -34,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV tokens/s through attention+impact+top-k; % of HBM / MFMA roofline"
 METRIC_DECODE = "KV tokens/s through one decode step; % of HBM roofline"
+METRIC_SELECT = "selected token-layers/s through K/V gather + scatter; % of HBM roofline"
+SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -133,6 +140,87 @@ def cpu_baseline(wl, budget_s=15.0):
             % (n - 1, len(wl.problems), wl.spec.name if wl.spec else "custom", elapsed)}
 
 
+def bench_select(args, torch, crkv, workloads):
+    """Gather + scatter of the selected keys' K/V rows (all layers, one launch
+    each); the roofline is the gather kernel's."""
+    base = SELECT_CONFIGS[args.config]
+    log("generating %s" % base)
+    wl = workloads.generate(base)
+    dev = "cuda:0"
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    problems = []
+    for p in wl.problems:
+        Q = up(p.Q)
+        problems.append(dict(Q=Q, chunk_K=[up(k) for k in p.K], chunk_V=[up(v) for v in p.V],
+                             chunk_len=list(p.lens), q_len=p.q_len, out=torch.empty_like(Q),
+                             impact=torch.empty(p.n_keys, dtype=torch.float32, device=dev)))
+    ks = [crkv.crkv_budget(p.n_doc, wl.r) for p in wl.problems]
+    idx = [torch.empty(k, dtype=torch.int32, device=dev) for k in ks]
+    crkv.crkv_attn_chunks_batched(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    crkv.crkv_topk_batched([pr["impact"] for pr in problems], [p.n_doc for p in wl.problems], ks, idx)
+    sels = [dict(chunk_K=pr["chunk_K"], chunk_V=pr["chunk_V"], chunk_len=pr["chunk_len"], idx=ix,
+                 K_sel=torch.empty((wl.H_kv, k, wl.d), dtype=torch.bfloat16, device=dev),
+                 V_sel=torch.empty((wl.H_kv, k, wl.d), dtype=torch.bfloat16, device=dev))
+            for pr, ix, k in zip(problems, idx, ks)]
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    batch = crkv.SelectBatch(sels)   # marshalled once: the same tensors every step
+
+    def step(events=None):
+        crkv.crkv_gather_kv(batch, wl.H_kv, wl.d, crkv.CRKV_BF16, timing_events=events)
+        crkv.crkv_scatter_kv(batch, wl.H_kv, wl.d, crkv.CRKV_BF16)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    selected = int(sum(ks))
+    row_bytes = wl.d * 2
+    gather_bytes = selected * wl.H_kv * 2 * row_bytes * 2     # K and V rows, read once and written once
+    achieved = gather_bytes / (k_ms * 1e-3) / 1e9
+    ms_per_step = wall * 1e3 / args.steps
+    rec = {"metric": METRIC_SELECT, "value": round(selected / (wall / args.steps), 1),
+           "unit": "selected token-layers/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": args.config, "layers": len(wl.problems), "H_kv": wl.H_kv, "d": wl.d,
+                      "selected_per_layer": ks[0], "chunks": len(wl.spec.chunk_lens),
+                      "chunk_len": wl.spec.chunk_lens[0], "q_len": wl.spec.q_len,
+                      "selection": "top-k of the attention impact, r = %g" % wl.r},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "kvsel_kernel<gather>", "kernel_ms": round(k_ms, 4),
+                        "alg_bytes_per_launch": gather_bytes}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        from oracle import kvsel
+        host_idx = [ix.cpu().numpy() for ix in idx]
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            for p, ix in zip(wl.problems, host_idx):
+                Kp, Vp = kvsel.gather_kv(p.K, p.V, p.lens, ix)
+                kvsel.scatter_kv(p.K, p.V, p.lens, ix, Kp, Vp)
+            reps += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": reps * selected / el, "unit": "selected token-layers/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "all %d layers, gather + scatter repeated %d times, %.1f s"
+                               % (len(wl.problems), reps, el)}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +256,9 @@ def main():
     if not os.path.exists(crkv.LIB_PATH):
         from attention_precomputed_chunk_amd import build as crkv_build
         crkv_build.build()
+    if args.config in SELECT_CONFIGS:
+        bench_select(args, torch, crkv, workloads)
+        return
 
     log("generating %s" % args.config)
     wl = workloads.generate(args.config)

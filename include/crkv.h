@@ -190,6 +190,37 @@ size_t crkv_decode_workspace_size(const crkv_problem *problems, int n_problems, 
 int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                    const crkv_opts *opts, int *kernel, int *row_tiles, int *workgroups);
 
+/*
+ * Moving the K/V rows of selected keys (CacheBlend summary, the three-phase
+ * flowchart: the K/V values of exactly the selected high-impact tokens are
+ * recomputed, and generation then runs on the fused cache). The recompute
+ * needs model weights and is the caller's; these calls move the rows:
+ *   crkv_gather_kv:  K_sel[h][j] = K_cat[h][idx[j]], V_sel likewise;
+ *   crkv_scatter_kv: K_cat[h][idx[j]] = K_sel[h][j], V_cat likewise;
+ * K_cat is the concatenation of the m + 1 segments (never formed). Rows are
+ * copied bit for bit in opts->dtype (opts->mode is ignored). idx holds
+ * positions in the concatenation: crkv_topk's output over the document keys
+ * can be passed as it is. A position outside [0, N) gathers a zero row and
+ * scatters nothing. Scatter indices must be distinct (with duplicates, which
+ * row lands is unspecified). Every selection of the array is done in one
+ * launch; opts->timing_events bracket it.
+ */
+typedef struct crkv_kv_select {
+    void *const *chunk_K;      /* host array of m + 1 device pointers, [H_kv][chunk_len[c]][d];
+                                  written by crkv_scatter_kv, only read by crkv_gather_kv */
+    void *const *chunk_V;
+    const int32_t *chunk_len;  /* host array of m + 1 lengths (>= 0) */
+    int m;
+    const int32_t *idx;        /* device int32 [k] */
+    int k;                     /* >= 0; 0 moves nothing */
+    void *K_sel;               /* device [H_kv][k][d], written by gather, read by scatter */
+    void *V_sel;
+} crkv_kv_select;
+
+/* All pointers 16-byte aligned; H_kv >= 1; d in {64, 128}; N < 2^30. */
+int crkv_gather_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts);
+int crkv_scatter_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts);
+
 const char *crkv_status_string(int status);
 const char *crkv_last_error(void);
 int crkv_version(void);

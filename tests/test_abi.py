@@ -178,3 +178,45 @@ def test_batch_marshals_once_and_plans_the_same(monkeypatch):
             == crkv.crkv_plan_info(probs, 8, 2, 128, mode="query", dtype=crkv.CRKV_BF16))
     assert (crkv.crkv_workspace_size(b, 8, 2, 128, dtype=crkv.CRKV_BF16)
             == crkv.crkv_workspace_size(probs, 8, 2, 128, dtype=crkv.CRKV_BF16))
+
+
+def _sel(k=4, lens=(8, 0, 5), idx=FAKE, K_sel=FAKE, V_sel=FAKE, chunk=FAKE, m=None):
+    m = len(lens) - 1 if m is None else m
+    n = len(lens)
+    keep = ((ctypes.c_void_p * n)(*[chunk if L else None for L in lens]),
+            (ctypes.c_void_p * n)(*[chunk if L else None for L in lens]),
+            (ctypes.c_int32 * n)(*lens))
+    return keep, crkv.crkv_kv_select(keep[0], keep[1], keep[2], m, idx, k, K_sel, V_sel)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", -1, -1), ("idx", None, -1), ("K_sel", None, -1), ("V_sel", FAKE + 8, -1),
+    ("chunk", FAKE + 4, -1), ("lens", (8, -1, 5), -1), ("m", -1, -1),
+])
+def test_gather_scatter_reject_invalid_arguments(crkv_lib, field, value, status):
+    kw = {field: value}
+    keep, s = _sel(**kw)
+    arr = (crkv.crkv_kv_select * 1)(s)
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    o.dtype = crkv.CRKV_BF16
+    assert crkv_lib.crkv_gather_kv(arr, 1, 2, 128, ctypes.byref(o)) == status
+    assert crkv_lib.crkv_scatter_kv(arr, 1, 2, 128, ctypes.byref(o)) == status
+
+
+def test_gather_scatter_shape_checks_and_empty_selection(crkv_lib):
+    keep, s = _sel()
+    arr = (crkv.crkv_kv_select * 1)(s)
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    assert crkv_lib.crkv_gather_kv(arr, 1, 2, 96, ctypes.byref(o)) == -2      # d
+    assert crkv_lib.crkv_gather_kv(arr, 1, 0, 128, ctypes.byref(o)) == -1     # H_kv
+    assert crkv_lib.crkv_gather_kv(arr, 0, 2, 128, ctypes.byref(o)) == -1     # no selections
+    o.dtype = 7
+    assert crkv_lib.crkv_gather_kv(arr, 1, 2, 128, ctypes.byref(o)) == -1
+    # k = 0 everywhere: valid, and nothing is enqueued (no device is touched)
+    o.dtype = crkv.CRKV_F32
+    keep0, s0 = _sel(k=0, idx=None, K_sel=None, V_sel=None)
+    arr0 = (crkv.crkv_kv_select * 1)(s0)
+    assert crkv_lib.crkv_gather_kv(arr0, 1, 2, 64, ctypes.byref(o)) == 0
+    assert crkv_lib.crkv_scatter_kv(arr0, 1, 2, 64, ctypes.byref(o)) == 0
