@@ -70,24 +70,33 @@ def algorithmic_work(wl):
     return nbytes, 4 * pairs * wl.H * wl.d, pairs
 
 
-def kernel_source_sha():
+# Sources each timed kernel is built from; a counter summary stays valid while
+# their hash matches.
+KERNEL_SOURCES = {
+    "attn": ("attn_bf16_wave.hip", "attn_bf16_pair.hip", "attn_bf16_common.h", "device_util.h",
+             "crkv_internal.h", "crkv_api.hip"),
+    "decode": ("decode_bf16.hip", "attn_bf16_common.h", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
+    "kvsel": ("kvsel.hip", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
+}
+
+
+def kernel_source_sha(kind="attn"):
     h = hashlib.sha256()
-    for f in ("attn_bf16_wave.hip", "attn_bf16_pair.hip", "attn_bf16_common.h", "device_util.h",
-              "crkv_internal.h", "crkv_api.hip"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "attention_precomputed_chunk_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "attn_%s_traffic.json" % config)
+def measured_traffic(config, kind="attn"):
+    """HBM bytes per launch of the timed kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kind, config))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_source_sha():
+    if t.get("kernel_sha") != kernel_source_sha(kind):
         return None
     return t.get("bytes_per_launch")
 
@@ -197,7 +206,8 @@ def bench_select(args, torch, crkv, workloads):
                       "chunk_len": wl.spec.chunk_lens[0], "q_len": wl.spec.q_len,
                       "selection": "top-k of the attention impact, r = %g" % wl.r},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(args.config, "kvsel"),
                         "kernel": "kvsel_kernel<gather>", "kernel_ms": round(k_ms, 4),
                         "alg_bytes_per_launch": gather_bytes}}
     if not args.no_cpu_baseline:
@@ -323,7 +333,7 @@ def main():
     achieved_gbs = nbytes / (k_ms * 1e-3) / 1e9
     achieved_tf = flops / (k_ms * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(args.config, "decode" if decode else "attn")
     hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
            "kernel": plan["kernel"] if decode else "attn_%s_kernel" % plan["kernel"],
