@@ -60,12 +60,16 @@ class crkv_kv_select(ctypes.Structure):
                 ("V_sel", ctypes.c_void_p)]
 
 
+class crkv_rope_seg(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_void_p), ("len", ctypes.c_int), ("delta", ctypes.c_int)]
+
+
 _lib = None
 
 DECLARED = ["crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
             "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
             "crkv_decode_chunks_batched", "crkv_decode_workspace_size", "crkv_gather_kv",
-            "crkv_scatter_kv",
+            "crkv_scatter_kv", "crkv_rope_shift",
             "crkv_status_string", "crkv_last_error", "crkv_version"]
 
 
@@ -115,6 +119,9 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [ctypes.POINTER(crkv_kv_select), c_int, c_int, c_int, ctypes.POINTER(crkv_opts)]
             f.restype = c_int
+        L.crkv_rope_shift.argtypes = [ctypes.POINTER(crkv_rope_seg), c_int, c_int, c_int, ctypes.c_double,
+                                      ctypes.POINTER(crkv_opts)]
+        L.crkv_rope_shift.restype = c_int
         L.crkv_status_string.argtypes = [c_int]
         L.crkv_status_string.restype = ctypes.c_char_p
         L.crkv_last_error.argtypes = []
@@ -333,6 +340,23 @@ def crkv_scatter_kv(sels: Sequence[dict], H_kv: int, d: int, dtype: int, stream=
     keep, arr = _selections(sels)
     o = make_opts(dtype, "query", stream, timing_events=timing_events)
     _check(lib().crkv_scatter_kv(arr, len(keep), H_kv, d, ctypes.byref(o)))
+
+
+class RopeBatch:
+    """Segments marshalled once for repeated crkv_rope_shift calls."""
+
+    def __init__(self, segs: Sequence[tuple]):
+        self.n = len(segs)
+        self.arr = (crkv_rope_seg * self.n)(*[crkv_rope_seg(_ptr(k), int(n), int(dl)) for k, n, dl in segs])
+
+
+def crkv_rope_shift(segs, H_kv: int, d: int, dtype: int, base: float = 10000.0,
+                    stream=None, timing_events=None):
+    """Rotate cached keys in place to new positions: segs is a list of
+    (K tensor [H_kv][len][d], len, delta), or a RopeBatch."""
+    b = segs if isinstance(segs, RopeBatch) else RopeBatch(segs)
+    o = make_opts(dtype, "query", stream, timing_events=timing_events)
+    _check(lib().crkv_rope_shift(b.arr, b.n, H_kv, d, float(base), ctypes.byref(o)))
 
 
 def crkv_budget(n_doc: int, r: float) -> int:

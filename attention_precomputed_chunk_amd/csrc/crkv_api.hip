@@ -35,6 +35,7 @@ hipError_t launch_topk_one(const TopkDesc &td, hipStream_t stream);
 hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream);
 hipError_t launch_topk_inline(const TopkDesc *descs, int n, hipStream_t stream);
 hipError_t launch_kvsel(bool scatter, const SelArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_rope_shift(int d, bool bf16, const RopeArgs &args, int n_items, hipStream_t stream);
 }  // namespace crkv
 
 using namespace crkv;
@@ -891,6 +892,100 @@ int run_sel(bool scatter, const crkv_kv_select *sel, int n, int H_kv, int d, con
     return e == hipSuccess ? CRKV_OK : hip_fail(e, scatter ? "scatter launch" : "gather launch");
 }
 
+// ------------------------------------------------------------ key re-positioning
+int run_rope(const crkv_rope_seg *segs, int n, int H_kv, int d, double base, const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = check_opts(o);
+    if (rc)
+        return rc;
+    if (n < 1 || !segs)
+        return fail(CRKV_E_INVAL, "n = %d segments (need >= 1, non-null array)", n);
+    if (H_kv < 1)
+        return fail(CRKV_E_INVAL, "H_kv = %d < 1", H_kv);
+    if (d != 64 && d != 128)
+        return fail(CRKV_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", d);
+    if (!(base > 1.0) || !std::isfinite(base))
+        return fail(CRKV_E_INVAL, "base = %g must be finite and > 1", base);
+    for (int i = 0; i < n; ++i) {
+        if (segs[i].len < 0)
+            return fail(CRKV_E_INVAL, "segment %d: len = %d < 0", i, segs[i].len);
+        if ((int64_t)segs[i].len * H_kv >= (int64_t(1) << 31))
+            return fail(CRKV_E_UNSUPPORTED, "segment %d: %lld rows (limit 2^31)", i,
+                        (long long)segs[i].len * H_kv);
+        if (segs[i].len > 0 && segs[i].delta != 0 && (!segs[i].K || !aligned16(segs[i].K)))
+            return fail(CRKV_E_INVAL, "segment %d: K must be non-null and 16-byte aligned", i);
+    }
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    const int half = d / 2;
+    std::vector<double> theta(half);   // base^(-2j/d), in double
+    for (int j = 0; j < half; ++j)
+        theta[j] = std::pow(base, -2.0 * j / d);
+    std::vector<RopeSeg> rs;
+    std::vector<size_t> table_of;      // per RopeSeg: its cos/sin table
+    std::vector<RopeItem> items;
+    std::vector<float> cs;
+    std::map<int, size_t> tables;      // one table per distinct shift
+    for (int i = 0; i < n; ++i) {
+        if (segs[i].len == 0 || segs[i].delta == 0)   // nothing moves
+            continue;
+        auto t = tables.find(segs[i].delta);
+        if (t == tables.end()) {
+            const size_t at = cs.size() / d;
+            cs.resize(cs.size() + d);
+            for (int j = 0; j < half; ++j) {   // angle delta * theta_j
+                const double ang = (double)segs[i].delta * theta[j];
+                cs[at * d + j] = (float)std::cos(ang);
+                cs[at * d + half + j] = (float)std::sin(ang);
+            }
+            t = tables.emplace(segs[i].delta, at).first;
+        }
+        const int idx = (int)rs.size();
+        RopeSeg r{};
+        r.K = segs[i].K;
+        r.rows = segs[i].len * H_kv;
+        rs.push_back(r);
+        table_of.push_back(t->second);
+        for (int r0 = 0; r0 < r.rows; r0 += kRopeRowsPerItem)
+            items.push_back(RopeItem{idx, r0});
+    }
+    if (items.empty())
+        return CRKV_OK;
+    const size_t off_segs = 0;
+    const size_t off_items = align_up(rs.size() * sizeof(RopeSeg), 256);
+    const size_t off_cs = align_up(off_items + items.size() * sizeof(RopeItem), 256);
+    const size_t bytes = align_up(off_cs + cs.size() * sizeof(float), 256);
+    PlanLease lease;
+    rc = plan_acquire(lease, bytes);
+    if (rc)
+        return rc;
+    for (size_t i = 0; i < rs.size(); ++i)
+        rs[i].cs = reinterpret_cast<const float *>(lease.dev + off_cs) + table_of[i] * d;
+    memset(lease.host, 0, bytes);
+    memcpy(lease.host + off_segs, rs.data(), rs.size() * sizeof(RopeSeg));
+    memcpy(lease.host + off_items, items.data(), items.size() * sizeof(RopeItem));
+    memcpy(lease.host + off_cs, cs.data(), cs.size() * sizeof(float));
+    rc = plan_commit(lease, bytes, stream);
+    hipError_t e = hipSuccess;
+    if (rc == CRKV_OK) {
+        RopeArgs args{};
+        args.segs = reinterpret_cast<const RopeSeg *>(lease.dev + off_segs);
+        args.items = reinterpret_cast<const RopeItem *>(lease.dev + off_items);
+        args.d = d;
+        args.bf16 = o.dtype == CRKV_BF16;
+        if (o.timing_events[0])
+            e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
+        if (e == hipSuccess)
+            e = launch_rope_shift(d, o.dtype == CRKV_BF16, args, (int)items.size(), stream);
+        if (e == hipSuccess && o.timing_events[1])
+            e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    }
+    plan_release(lease, stream);
+    if (rc)
+        return rc;
+    return e == hipSuccess ? CRKV_OK : hip_fail(e, "key re-positioning launch");
+}
+
 extern "C" {
 
 void crkv_opts_init(crkv_opts *opts)
@@ -1161,6 +1256,11 @@ int crkv_gather_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv
 int crkv_scatter_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts)
 {
     return run_sel(true, sel, n, H_kv, d, opts);
+}
+
+int crkv_rope_shift(const crkv_rope_seg *segs, int n, int H_kv, int d, double base, const crkv_opts *opts)
+{
+    return run_rope(segs, n, H_kv, d, base, opts);
 }
 
 }  // extern "C"

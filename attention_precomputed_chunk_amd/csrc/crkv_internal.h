@@ -167,4 +167,28 @@ struct SelArgs {
 };
 static_assert(sizeof(SelSeg) == 32 && sizeof(SelProb) == 48 && sizeof(SelItem) == 8, "table layout");
 
+// ---------------------------------------------------------------- key re-positioning (rotary embedding)
+constexpr int kRopeThreads = 256;
+constexpr int kRopeRowsPerItem = 256;   // rows ([H_kv * len] of a segment) per workgroup
+
+struct RopeSeg {
+    void *K;                  // [H_kv][len][d], rotated in place
+    const float *cs;          // cos of the d/2 angles, then their sin
+    int32_t rows;             // H_kv * len
+    int32_t pad;
+};
+
+struct RopeItem {
+    int32_t seg;
+    int32_t row0;
+};
+
+struct RopeArgs {
+    const RopeSeg *segs;
+    const RopeItem *items;
+    int32_t d;
+    int32_t bf16;
+};
+static_assert(sizeof(RopeSeg) == 24 && sizeof(RopeItem) == 8, "table layout");
+
 }  // namespace crkv

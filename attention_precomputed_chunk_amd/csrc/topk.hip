@@ -164,27 +164,59 @@ __device__ void topk_body(const TopkDesc td)
         const unsigned long long packed =
             ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
         if (kk > T) {
-            sel[atomicAdd(&s_gt, 1)] = packed;
+            sel[atomicAdd(&s_gt, 1)] = packed;   // any order: the sort orders them
         } else if (kk == T) {
             if (rank < remaining)
                 sel[n_gt + rank] = packed;
             ++rank;
         }
     }
-    int P = 1;
+    int P = 128;   // at least one 128-entry block (see the sort)
     while (P < k)
         P <<= 1;
     for (int i = k + tid; i < P; i += kTopkThreads)
         sel[i] = 0ull;   // below every real entry
     __syncthreads();
 
-    // Bitonic sort, descending. Thread t compares pair t (and t + 1024, ...).
-    // For strides below 64 the pairs of each 128-element block all belong to
-    // one wave, whose LDS accesses execute in order, so those stages only need
-    // a wave-level ordering point; a workgroup barrier follows every stage
-    // with a larger stride and the last stage of every size.
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+    // Bitonic sort, descending, of P = 2^j >= 128 entries. Stages whose
+    // stride is at least 128 compare entries of different 128-entry blocks
+    // and go through LDS with a barrier each. The others stay inside a block:
+    // wave w holds block w (and w + 16, ...) in registers, lane l entries l
+    // and l + 64, and such a run of stages is done with lane shuffles and no
+    // LDS traffic.
+    auto reg_run = [&](int size_lo, int size_hi, int stride_first) {
+        for (int blk = wave; blk < P / 128; blk += kTopkWaves) {
+            const int base = blk * 128;
+            unsigned long long x0 = sel[base + lane], x1 = sel[base + lane + 64];
+            const int i0 = base + lane, i1 = i0 + 64;
+            for (int size = size_lo; size <= size_hi; size <<= 1) {
+                for (int stride = (size == size_lo ? stride_first : size >> 1); stride > 0; stride >>= 1) {
+                    if (stride == 64) {   // pair (i0, i1) of this lane
+                        const bool desc = (i0 & size) == 0;
+                        if ((x0 < x1) == desc) {
+                            const unsigned long long t = x0;
+                            x0 = x1;
+                            x1 = t;
+                        }
+                    } else {
+                        const unsigned long long y0 = __shfl_xor(x0, stride), y1 = __shfl_xor(x1, stride);
+                        const bool lo = (lane & stride) == 0;
+                        // the lower position of a pair keeps the larger entry in a descending block
+                        const bool max0 = lo == ((i0 & size) == 0), max1 = lo == ((i1 & size) == 0);
+                        x0 = max0 ? (x0 > y0 ? x0 : y0) : (x0 < y0 ? x0 : y0);
+                        x1 = max1 ? (x1 > y1 ? x1 : y1) : (x1 < y1 ? x1 : y1);
+                    }
+                }
+            }
+            sel[base + lane] = x0;
+            sel[base + lane + 64] = x1;
+        }
+        __syncthreads();
+    };
+    reg_run(2, 128, 1);   // every stage of the sizes up to 128
+    for (int size = 256; size <= P; size <<= 1) {
+        int stride = size >> 1;
+        for (; stride >= 128; stride >>= 1) {
             for (int t = tid; t < P / 2; t += kTopkThreads) {
                 const int lo = 2 * t - (t & (stride - 1));
                 const int hi = lo + stride;
@@ -195,14 +227,9 @@ __device__ void topk_body(const TopkDesc td)
                     sel[hi] = x;
                 }
             }
-            if (stride >= 64 || stride == 1) {
-                __syncthreads();   // cross-wave stage, or the next size starts with one
-            } else {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            }
+            __syncthreads();
         }
+        reg_run(size, size, 64);
     }
     __syncthreads();
     for (int i = tid; i < k; i += kTopkThreads)

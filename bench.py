@@ -19,6 +19,11 @@ layer's selected keys (the top-1500 of the default workload's impact, found
 once before timing): one gather launch into packed buffers and one scatter
 launch back into the segments.
 
+With --config llama3_8b_rope_shift_32l a step moves the cached keys of every
+document chunk of the 32 layers from positions 0 .. 2499 to their place in the
+concatenation (offsets 2500, 5000, 7500; the first chunk stays): one
+rotary re-positioning launch over all of them.
+
 Prints one JSON line. The roofline object is for the attention kernel alone,
 timed with HIP events recorded on its stream around every launch.
 """
@@ -41,6 +46,8 @@ METRIC = "KV tokens/s through attention+impact+top-k; % of HBM / MFMA roofline"
 METRIC_DECODE = "KV tokens/s through one decode step; % of HBM roofline"
 METRIC_SELECT = "selected token-layers/s through K/V gather + scatter; % of HBM roofline"
 SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
+METRIC_ROPE = "re-positioned key-layers/s (rotary shift of cached keys); % of HBM roofline"
+ROPE_CONFIGS = {"llama3_8b_rope_shift_32l": "llama3_8b_gqa_32l"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -77,6 +84,7 @@ KERNEL_SOURCES = {
              "crkv_internal.h", "crkv_api.hip"),
     "decode": ("decode_bf16.hip", "attn_bf16_common.h", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
     "kvsel": ("kvsel.hip", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
+    "rope": ("rope.hip", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
 }
 
 
@@ -231,6 +239,73 @@ def bench_select(args, torch, crkv, workloads):
     print(json.dumps(rec), flush=True)
 
 
+def bench_rope(args, torch, crkv, workloads):
+    """Rotary re-positioning of every document chunk's cached keys (all layers,
+    one launch)."""
+    base = ROPE_CONFIGS[args.config]
+    log("generating %s" % base)
+    wl = workloads.generate(base)
+    dev = "cuda:0"
+    segs = []
+    for p in wl.problems:
+        off = 0
+        for c in range(len(p.lens) - 1):   # document chunks; each was built at positions 0 ..
+            K = torch.from_numpy(p.K[c].view(np.int16)).to(dev).view(torch.bfloat16)
+            segs.append((K, p.lens[c], off))
+            off += p.lens[c]
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    batch = crkv.RopeBatch(segs)   # marshalled once: the same tensors every step
+
+    def step(events=None):
+        crkv.crkv_rope_shift(batch, wl.H_kv, wl.d, crkv.CRKV_BF16, timing_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    moved = int(sum(n for _, n, dl in segs if dl != 0))
+    nbytes = moved * wl.H_kv * wl.d * 2 * 2     # every moved key row read once and written once
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    rec = {"metric": METRIC_ROPE, "value": round(moved / (wall / args.steps), 1),
+           "unit": "key-layers/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": args.config, "layers": len(wl.problems), "H_kv": wl.H_kv, "d": wl.d,
+                      "chunks": len(wl.spec.chunk_lens), "chunk_len": wl.spec.chunk_lens[0],
+                      "shifts": sorted(set(dl for _, _, dl in segs)), "base": 10000.0},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config, "rope"),
+                        "kernel": "rope_shift_kernel", "kernel_ms": round(k_ms, 4), "alg_bytes_per_launch": nbytes}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        from oracle import rope
+        done, t0 = 0, time.perf_counter()
+        for p in wl.problems:
+            off = 0
+            for c in range(len(p.lens) - 1):
+                if off:
+                    rope.rope_shift(p.K[c], off, "bf16")
+                    done += p.lens[c]
+                off += p.lens[c]
+            if time.perf_counter() - t0 > 10.0:
+                break
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done / el, "unit": "key-layers/s", "cores": 1, "kind": "oracle",
+                               "sample": "%d moved chunks' keys of the first layers, %.1f s" % (done // 2500, el)}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +343,9 @@ def main():
         crkv_build.build()
     if args.config in SELECT_CONFIGS:
         bench_select(args, torch, crkv, workloads)
+        return
+    if args.config in ROPE_CONFIGS:
+        bench_rope(args, torch, crkv, workloads)
         return
 
     log("generating %s" % args.config)

@@ -221,6 +221,33 @@ typedef struct crkv_kv_select {
 int crkv_gather_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts);
 int crkv_scatter_kv(const crkv_kv_select *sel, int n, int H_kv, int d, const crkv_opts *opts);
 
+/*
+ * Moving cached keys to new positions under rotary position embedding
+ * (TurboRAG summary, implementation notes: with rotary embedding the
+ * position IDs a chunk's cache was built with must agree with those it is
+ * used at, e.g. a chunk precomputed at positions 0 .. len-1 and placed at
+ * offset o of the concatenation). The pages give no formula; this is the
+ * standard rotary embedding in the rotate-half arrangement. For each key row
+ * x of a segment and i < d/2, with a_i = delta * base^(-2i/d):
+ *   y_i       = x_i cos(a_i) - x_{i+d/2} sin(a_i)
+ *   y_{i+d/2} = x_{i+d/2} cos(a_i) + x_i sin(a_i)
+ * in place, in opts->dtype (float32 arithmetic, cos and sin evaluated in
+ * double on the host, one rounding to the stored type). Rotations compose:
+ * delta moves keys by delta positions, -delta moves them back. Segments with
+ * len == 0 or delta == 0 are left untouched (no memory traffic). V has no
+ * positional rotation and is not an argument. opts->mode is ignored;
+ * opts->timing_events bracket the launch.
+ */
+typedef struct crkv_rope_seg {
+    void *K;     /* device [H_kv][len][d], rotated in place; 16-byte aligned */
+    int len;     /* >= 0 */
+    int delta;   /* new position minus old position */
+} crkv_rope_seg;
+
+/* All segments in one launch. H_kv >= 1, d in {64, 128}, base finite > 1
+ * (10000 in the common models), H_kv * len < 2^31. */
+int crkv_rope_shift(const crkv_rope_seg *segs, int n, int H_kv, int d, double base, const crkv_opts *opts);
+
 const char *crkv_status_string(int status);
 const char *crkv_last_error(void);
 int crkv_version(void);

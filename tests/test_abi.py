@@ -220,3 +220,23 @@ def test_gather_scatter_shape_checks_and_empty_selection(crkv_lib):
     arr0 = (crkv.crkv_kv_select * 1)(s0)
     assert crkv_lib.crkv_gather_kv(arr0, 1, 2, 64, ctypes.byref(o)) == 0
     assert crkv_lib.crkv_scatter_kv(arr0, 1, 2, 64, ctypes.byref(o)) == 0
+
+
+def test_rope_shift_rejects_invalid_arguments(crkv_lib):
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    o.dtype = crkv.CRKV_BF16
+    ok = (crkv.crkv_rope_seg * 1)(crkv.crkv_rope_seg(FAKE, 16, 5))
+    L = crkv_lib
+    assert L.crkv_rope_shift(ok, 1, 2, 96, 10000.0, ctypes.byref(o)) == -2        # d
+    assert L.crkv_rope_shift(ok, 1, 0, 128, 10000.0, ctypes.byref(o)) == -1       # H_kv
+    assert L.crkv_rope_shift(ok, 1, 2, 128, 1.0, ctypes.byref(o)) == -1           # base
+    assert L.crkv_rope_shift(ok, 1, 2, 128, float("inf"), ctypes.byref(o)) == -1
+    assert L.crkv_rope_shift(ok, 0, 2, 128, 10000.0, ctypes.byref(o)) == -1       # n
+    for seg in (crkv.crkv_rope_seg(FAKE, -1, 5), crkv.crkv_rope_seg(None, 16, 5),
+                crkv.crkv_rope_seg(FAKE + 8, 16, 5)):
+        bad = (crkv.crkv_rope_seg * 1)(seg)
+        assert L.crkv_rope_shift(bad, 1, 2, 128, 10000.0, ctypes.byref(o)) == -1
+    # nothing moves: delta 0, or an empty segment (valid; nothing is enqueued)
+    idle = (crkv.crkv_rope_seg * 2)(crkv.crkv_rope_seg(None, 16, 0), crkv.crkv_rope_seg(None, 0, 7))
+    assert L.crkv_rope_shift(idle, 2, 2, 128, 10000.0, ctypes.byref(o)) == 0
