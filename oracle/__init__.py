@@ -21,7 +21,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 MODE_CODE = {"query": 0, "cross": 1, "all": 2}
-DTYPE_CODE = {"f32": 0, "bf16": 1}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f64": 2}
 
 
 def _stale() -> bool:

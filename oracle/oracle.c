@@ -9,7 +9,8 @@
  *
  * Everything is computed in float64 with plain loops, in the order the pages
  * state the method. Inputs (fp32 or bf16 bit patterns) are widened exactly to
- * float64 before any arithmetic.
+ * float64 before any arithmetic; float64 inputs (values of a dequantised
+ * cache, which need not fit float32) are taken as they are.
  *
  * Sources (the pages are blog summaries of the papers):
  *  - TurboRAG summary, "Precomputing the KV cache": the combined K (and V) is
@@ -46,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 enum { OR_QUERY_ROWS = 0, OR_CROSS_DOC = 1, OR_ALL_ROWS = 2 };
 
 /* Exact widening of one stored element to float64. */
@@ -58,6 +59,8 @@ static double widen(const void *base, int dtype, size_t i)
         memcpy(&f, &bits, sizeof f);
         return (double)f;
     }
+    if (dtype == OR_F64)
+        return ((const double *)base)[i];
     return (double)((const float *)base)[i];
 }
 

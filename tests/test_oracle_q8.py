@@ -1,0 +1,168 @@
+"""Pins of the 8-bit K/V format oracle against what its definition fixes:
+rows with a power-of-two scale whose codes are the textbook round-half-even of
+the input, brute-force nearest code on tiny inputs, the error bound, the
+extreme element, zero rows, sign and power-of-two scale symmetry, the buffer
+layout, a decode step over a cache the format stores exactly (equal to the
+decode over the original values), and planted mistakes."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import q8
+import workloads
+
+
+def f32_to_bf16_bits(x):
+    return workloads.round_bf16(np.asarray(x, dtype=np.float32))
+
+
+def test_unit_scale_is_round_half_even():
+    """max |x| = 127 gives scale exactly 1, so the codes are the integers
+    nearest to x, halves to the even one."""
+    x = np.array([[127.0, -64.5, 32.5, 0.5, 1.5, -2.5, 3.25, 0.0]], dtype=np.float32)
+    codes, scale = q8.quantize(x, "f32")
+    assert scale[0] == np.float32(1.0)
+    assert codes[0].tolist() == [127, -64, 32, 0, 2, -2, 3, 0]
+
+
+def test_scale_two():
+    x = np.array([[-254.0, 5.0, 7.0, -3.0, 100.5, 2.0]], dtype=np.float32)
+    codes, scale = q8.quantize(x, "f32")
+    assert scale[0] == np.float32(2.0)
+    # x / 2 = -127, 2.5, 3.5, -1.5, 50.25, 1
+    assert codes[0].tolist() == [-127, 2, 4, -2, 50, 1]
+
+
+def test_decision_in_float32():
+    """77 / 127 rounded to float32, then 38.5 divided by it, is exactly 63.5 in
+    float32 (a tie, to the even code 64); the exact quotient is just below
+    63.5 (code 63). The code must be the float32 one, the precision the
+    kernel decides in."""
+    x = np.array([[77.0, 38.5, -38.5, 1.0]], dtype=np.float32)
+    codes, scale = q8.quantize(f32_to_bf16_bits(x), "bf16")
+    s = np.float32(np.float32(77.0) / np.float32(127.0))
+    assert scale[0] == s and np.float32(np.float32(38.5) / s) == np.float32(63.5)
+    assert 38.5 / float(s) < 63.5
+    assert codes[0].tolist() == [127, 64, -64, 2]
+
+
+def brute_codes(x32, scale):
+    """For each element, the code c in [-127, 127] nearest to x / scale computed
+    in float32, found by trying all 255 (ties: the even one)."""
+    out = []
+    for v in x32:
+        t = np.float32(v) / np.float32(scale)
+        best = None
+        for c in range(-127, 128):
+            dist = abs(float(t) - c)
+            if best is None or dist < best[0] - 1e-12 or (abs(dist - best[0]) <= 1e-12 and c % 2 == 0):
+                best = (dist, c)
+        out.append(best[1])
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_nearest_code(seed):
+    rng = np.random.default_rng(seed)
+    d = 16
+    x = rng.standard_normal((3, d)).astype(np.float32) * np.float32(rng.uniform(0.01, 50))
+    x[1, 3] = 0.0
+    bits = f32_to_bf16_bits(x)
+    codes, scales = q8.quantize(bits, "bf16")
+    xw = (bits.astype(np.uint32) << 16).view(np.float32)
+    for r in range(3):
+        a = np.max(np.abs(xw[r]))
+        assert scales[r] == np.float32(a) / np.float32(127)
+        assert codes[r].tolist() == brute_codes(xw[r], scales[r])
+
+
+def test_error_bound_extreme_and_range():
+    wl = workloads.custom(11, [300, 7], 1, 4, 2, 128, dtype="bf16", k_outliers=4, gen_len=20)
+    for k in wl.problems[0].K:
+        codes, scales = q8.quantize(k, "bf16")
+        x = workloads.widen(k, "bf16")
+        deq = q8.dequantize(codes, scales)
+        assert codes.dtype == np.int8 and int(np.abs(codes.astype(int)).max()) <= 127
+        # nearest code to the float32 quotient t = (x / scale)(1 + e), |e| <= 2^-24,
+        # |x / scale| <= 127: at most half a step plus 128 * 2^-24 steps
+        assert np.all(np.abs(x - deq) <= (0.5 + 128 * 2.0 ** -24) * scales[..., None])
+        # the largest magnitude of every row lands on +-127
+        arg = np.argmax(np.abs(x), axis=-1)
+        top = np.take_along_axis(codes.astype(int), arg[..., None], axis=-1)[..., 0]
+        assert np.all(np.abs(top) == 127)
+
+
+def test_zero_rows_sign_and_power_of_two_symmetry():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    x[2] = 0.0
+    c, s = q8.quantize(x, "f32")
+    assert s[2] == 0 and not c[2].any() and not q8.dequantize(c, s)[2].any()
+    cn, sn = q8.quantize(-x, "f32")
+    assert np.array_equal(cn, -c) and np.array_equal(sn, s)
+    c8, s8 = q8.quantize(x * np.float32(8.0), "f32")
+    assert np.array_equal(c8, c) and np.array_equal(s8, s * np.float32(8.0))
+
+
+def test_buffer_layout():
+    rng = np.random.default_rng(4)
+    H_kv, n, d = 3, 5, 64
+    k = f32_to_bf16_bits(rng.standard_normal((H_kv, n, d)))
+    codes, scales = q8.quantize(k, "bf16")
+    buf = q8.pack(codes, scales)
+    assert buf.size == q8.nbytes(H_kv, n, d) == H_kv * n * d + 4 * H_kv * n
+    assert buf[:H_kv * n * d].view(np.int8).reshape(H_kv, n, d)[1, 2, 7] == codes[1, 2, 7]
+    assert buf[H_kv * n * d:].view(np.float32)[1 * n + 4] == scales[1, 4]
+    c2, s2 = q8.unpack(buf, H_kv, n, d)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+def test_decode_over_an_exactly_stored_cache():
+    """K/V rows of integers in [-127, 127] whose largest magnitude is 127 are
+    stored exactly (scale 1), so the decode step over the format equals the
+    decode step over the original bf16 values."""
+    wl = workloads.custom(5, [40, 0, 33], 1, 8, 2, 64, dtype="bf16", gen_len=6)
+    p = wl.problems[0]
+    rng = np.random.default_rng(9)
+    for segs in (p.K, p.V):
+        for i, s in enumerate(segs):
+            v = rng.integers(-127, 128, size=s.shape).astype(np.float32)
+            if v.size:
+                v[..., 0] = 127.0
+            segs[i] = f32_to_bf16_bits(v / np.float32(16.0)) if segs is p.V else f32_to_bf16_bits(v)
+    # V rows are integers / 16: still exact (scale 127/16/127 = 1/16)
+    kq, vq = q8.quantize_problem(p)
+    for (c, s), k in zip(kq, p.K):
+        assert np.array_equal(q8.dequantize(c, s), workloads.widen(k, "bf16"))
+    ref, _, _ = oracle.attn(p, wl.H, wl.H_kv, wl.d, "bf16", "query")
+    got = q8.decode(p, wl.H, wl.H_kv, wl.d, kq, vq)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mutant", ["half_away", "scale_128", "no_float32_quotient"])
+def test_pins_catch_planted_mistakes(mutant, monkeypatch):
+    real = q8.quantize
+
+    def bad(x, dtype="bf16"):
+        xf = q8._f32(x, dtype)
+        amax = np.max(np.abs(xf), axis=-1)
+        if mutant == "scale_128":
+            scale = (amax / np.float32(128)).astype(np.float32)
+        else:
+            scale = (amax / np.float32(127)).astype(np.float32)
+        safe = np.where(scale > 0, scale, 1).astype(np.float32)
+        if mutant == "no_float32_quotient":   # quotient in float64: other ties near .5
+            t = xf.astype(np.float64) / safe.astype(np.float64)[..., None]
+            codes = np.rint(t)
+        else:
+            t = (xf / safe[..., None]).astype(np.float32)
+            codes = np.sign(t) * np.floor(np.abs(t) + 0.5) if mutant == "half_away" else np.rint(t)
+        codes = np.where(scale[..., None] > 0, np.clip(codes, -127, 127), 0).astype(np.int8)
+        return codes, scale
+
+    monkeypatch.setattr(q8, "quantize", bad)
+    with pytest.raises(AssertionError):
+        test_unit_scale_is_round_half_even()
+        test_scale_two()
+        test_decision_in_float32()
+    monkeypatch.setattr(q8, "quantize", real)
