@@ -9,18 +9,26 @@ cache dominates the time to first token and that caches can be encoded into a
 much smaller form (its figures: 3.5-4.3x smaller), but the page gives no codec.
 The format here is this repository's own (parity unpinned against the pages);
 it keeps the part of the idea that pays where the path is bound by HBM: fewer
-bytes per cached key. Each row (one token of one KV head, d values x_t, bf16
-widened exactly to float32) becomes a float32 scale and d signed 8-bit codes:
+bytes per cached key. Values (bf16 widened exactly to float32) become signed
+8-bit codes with float32 scales, one scale per group:
 
-    a      = max_t |x_t|
+    a      = max over the group of |x|
     scale  = fl32(a / 127)                                  (0 when a = 0)
-    code_t = clamp(round_half_even(fl32(x_t / scale)), -127, 127)
+    code   = clamp(round_half_even(fl32(x / scale)), -127, 127)
 
 with both divisions in float32 (IEEE, round to nearest even), so the integer
 decision is taken in the precision the kernel takes it. The dequantised value
-is code_t * scale, exact in float64. A segment [H_kv][len][d] is stored as one
-buffer: the codes [H_kv][len][d] (int8), then the scales [H_kv][len] (float32)
-at byte offset H_kv * len * d.
+is code * scale, exact in float64. The groups differ for K and V:
+
+* K ("k"): one scale per (KV head, channel) over the segment's tokens. Cached
+  keys carry a few channels of much larger magnitude (the synthetic workloads
+  model them as outlier channels), and a scale per channel keeps them from
+  coarsening the other channels' steps.
+* V ("v"): one scale per (KV head, token) over the d channels.
+
+A segment [H_kv][len][d] is stored as one buffer: the codes [H_kv][len][d]
+(int8), then the scales at byte offset H_kv * len * d, float32 [H_kv][d] for
+K or [H_kv][len] for V. A segment with len = 0 occupies no bytes.
 
 A decode step over quantised segments is the decode step (the newest token's
 row over every cached key, TurboRAG summary's generation loop) over the
@@ -41,40 +49,57 @@ def _f32(x, dtype: str) -> np.ndarray:
     return np.asarray(x, dtype=np.float32)
 
 
-def quantize(x, dtype: str = "bf16"):
-    """Rows [..., d] -> (codes int8 [..., d], scales float32 [...])."""
+def _axis(kind: str) -> int:
+    if kind not in ("k", "v"):
+        raise ValueError(kind)
+    return -2 if kind == "k" else -1
+
+
+def quantize(x, kind: str, dtype: str = "bf16"):
+    """[H_kv][len][d] -> (codes int8 [H_kv][len][d], scales float32:
+    [H_kv][d] for kind "k" (per channel), [H_kv][len] for "v" (per token))."""
+    ax = _axis(kind)
     xf = _f32(x, dtype)
-    amax = np.max(np.abs(xf), axis=-1)                         # exact
+    if xf.shape[-2] == 0:
+        sc_shape = xf.shape[:-2] + ((xf.shape[-1],) if kind == "k" else (0,))
+        return np.zeros(xf.shape, dtype=np.int8), np.zeros(sc_shape, dtype=np.float32)
+    amax = np.max(np.abs(xf), axis=ax)                         # exact
     scale = (amax / np.float32(CODE_MAX)).astype(np.float32)   # one float32 division
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    q = (xf / safe[..., None]).astype(np.float32)              # float32 division per element
+    safe = np.expand_dims(np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32), ax)
+    q = (xf / safe).astype(np.float32)                         # float32 division per element
     codes = np.clip(np.rint(q), -CODE_MAX, CODE_MAX)           # rint: ties to even
-    codes = np.where(scale[..., None] > 0, codes, 0.0).astype(np.int8)
+    codes = np.where(np.expand_dims(scale, ax) > 0, codes, 0.0).astype(np.int8)
     return codes, scale
 
 
-def dequantize(codes, scales) -> np.ndarray:
+def dequantize(codes, scales, kind: str) -> np.ndarray:
     """code * scale in float64 (exact: at most 8 + 24 significant bits)."""
-    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+    return np.asarray(codes, dtype=np.float64) * np.expand_dims(np.asarray(scales, dtype=np.float64), _axis(kind))
 
 
-def nbytes(H_kv: int, n: int, d: int) -> int:
-    return H_kv * n * d + 4 * H_kv * n
+def nbytes(H_kv: int, n: int, d: int, kind: str) -> int:
+    if n == 0:
+        return 0
+    return H_kv * n * d + 4 * H_kv * (d if kind == "k" else n)
 
 
 def pack(codes, scales) -> np.ndarray:
-    """One segment buffer (uint8): codes [H_kv][len][d], then scales [H_kv][len]."""
+    """One segment buffer (uint8): the codes, then the scales."""
     codes = np.ascontiguousarray(codes, dtype=np.int8)
+    if codes.size == 0:
+        return np.zeros(0, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
     return np.concatenate([codes.reshape(-1).view(np.uint8), scales.reshape(-1).view(np.uint8)])
 
 
-def unpack(buf, H_kv: int, n: int, d: int):
+def unpack(buf, H_kv: int, n: int, d: int, kind: str):
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
-    if buf.size != nbytes(H_kv, n, d):
-        raise ValueError("segment buffer holds %d bytes, the format needs %d" % (buf.size, nbytes(H_kv, n, d)))
+    if buf.size != nbytes(H_kv, n, d, kind):
+        raise ValueError("segment buffer holds %d bytes, the format needs %d" % (buf.size, nbytes(H_kv, n, d, kind)))
+    if n == 0:
+        return quantize(np.zeros((H_kv, 0, d), dtype=np.float32), kind, "f32")
     codes = buf[: H_kv * n * d].view(np.int8).reshape(H_kv, n, d)
-    scales = buf[H_kv * n * d:].view(np.float32).reshape(H_kv, n)
+    scales = buf[H_kv * n * d:].view(np.float32).reshape(H_kv, d if kind == "k" else n)
     return codes, scales
 
 
@@ -86,8 +111,8 @@ class DequantProblem:
     """A decode problem whose segments are the dequantised cache (float64)."""
 
     def __init__(self, problem, kq, vq):
-        self.K = [dequantize(c, s) for c, s in kq]
-        self.V = [dequantize(c, s) for c, s in vq]
+        self.K = [dequantize(c, s, "k") for c, s in kq]
+        self.V = [dequantize(c, s, "v") for c, s in vq]
         self.lens = list(problem.lens)
         self.q_len = problem.q_len
         self.m = problem.m
@@ -96,8 +121,8 @@ class DequantProblem:
 
 def quantize_problem(problem, dtype: str = "bf16"):
     """(codes, scales) for every segment's K and V."""
-    kq = [quantize(k, dtype) for k in problem.K]
-    vq = [quantize(v, dtype) for v in problem.V]
+    kq = [quantize(k, "k", dtype) for k in problem.K]
+    vq = [quantize(v, "v", dtype) for v in problem.V]
     return kq, vq
 
 
