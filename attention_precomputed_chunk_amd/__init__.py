@@ -11,6 +11,8 @@ Functions carry the C names:
 * ``crkv_attn_chunks_batched(problems, H, H_kv, d, ...)``
 * ``crkv_topk(impact, n, k, idx, ...)`` and ``crkv_topk_batched(...)``
 * ``crkv_decode_chunks_batched(problems, H, H_kv, d, ...)`` (one decode step)
+* ``crkv_quantize_q8(...)``, ``crkv_q8_bytes(...)`` (the 8-bit K/V segment format;
+  ``crkv_decode_chunks_batched(..., dtype=CRKV_KV_Q8)`` reads it)
 * ``crkv_budget(n_doc, r)``, ``crkv_workspace_size(...)``, ``crkv_plan_info(...)``,
   ``crkv_version()``
 """
@@ -31,6 +33,7 @@ CRKV_E_HIP = -3
 CRKV_E_NOMEM = -4
 CRKV_F32 = 0
 CRKV_BF16 = 1
+CRKV_KV_Q8 = 2
 MODES = {"query": 0, "cross": 1, "all": 2}
 
 
@@ -64,9 +67,17 @@ class crkv_rope_seg(ctypes.Structure):
     _fields_ = [("K", ctypes.c_void_p), ("len", ctypes.c_int), ("delta", ctypes.c_int)]
 
 
+CRKV_Q8_K = 0
+CRKV_Q8_V = 1
+
+
+class crkv_q8_seg(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("q8", ctypes.c_void_p), ("len", ctypes.c_int), ("kind", ctypes.c_int)]
+
+
 _lib = None
 
-DECLARED = ["crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
+DECLARED = ["crkv_q8_bytes", "crkv_quantize_q8", "crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
             "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
             "crkv_decode_chunks_batched", "crkv_decode_workspace_size", "crkv_gather_kv",
             "crkv_scatter_kv", "crkv_rope_shift",
@@ -122,6 +133,10 @@ def lib():
         L.crkv_rope_shift.argtypes = [ctypes.POINTER(crkv_rope_seg), c_int, c_int, c_int, ctypes.c_double,
                                       ctypes.POINTER(crkv_opts)]
         L.crkv_rope_shift.restype = c_int
+        L.crkv_q8_bytes.argtypes = [c_int, c_int, c_int, c_int]
+        L.crkv_q8_bytes.restype = ctypes.c_size_t
+        L.crkv_quantize_q8.argtypes = [ctypes.POINTER(crkv_q8_seg), c_int, c_int, c_int, ctypes.POINTER(crkv_opts)]
+        L.crkv_quantize_q8.restype = c_int
         L.crkv_status_string.argtypes = [c_int]
         L.crkv_status_string.restype = ctypes.c_char_p
         L.crkv_last_error.argtypes = []
@@ -246,17 +261,20 @@ def crkv_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int, mod
 
 
 def crkv_decode_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int, stream=None,
-                               workspace=None, workspace_bytes: int = 0, timing_events=None):
+                               workspace=None, workspace_bytes: int = 0, timing_events=None,
+                               dtype: int = CRKV_BF16):
     """One decode step (q_len = 1 per problem); dicts as for crkv_attn_chunks_batched,
-    'impact' may be None."""
+    'impact' may be None. dtype=CRKV_KV_Q8: chunk_K / chunk_V are segment
+    buffers in the 8-bit format (crkv_quantize_q8)."""
     keep, arr = _problems(problems)
-    o = make_opts(CRKV_BF16, "query", stream, workspace, workspace_bytes, timing_events)
+    o = make_opts(dtype, "query", stream, workspace, workspace_bytes, timing_events)
     _check(lib().crkv_decode_chunks_batched(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
 
 
-def crkv_decode_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int) -> int:
+def crkv_decode_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int,
+                               dtype: int = CRKV_BF16) -> int:
     keep, arr = _problems(problems)
-    o = make_opts(CRKV_BF16, "query", stream=0)
+    o = make_opts(dtype, "query", stream=0)
     return int(lib().crkv_decode_workspace_size(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
 
 
@@ -357,6 +375,29 @@ def crkv_rope_shift(segs, H_kv: int, d: int, dtype: int, base: float = 10000.0,
     b = segs if isinstance(segs, RopeBatch) else RopeBatch(segs)
     o = make_opts(dtype, "query", stream, timing_events=timing_events)
     _check(lib().crkv_rope_shift(b.arr, b.n, H_kv, d, float(base), ctypes.byref(o)))
+
+
+def crkv_q8_bytes(H_kv: int, n: int, d: int, kind: int) -> int:
+    """Bytes of one segment of n keys in the 8-bit format (kind CRKV_Q8_K or CRKV_Q8_V)."""
+    return int(lib().crkv_q8_bytes(H_kv, n, d, kind))
+
+
+class Q8Batch:
+    """Segments marshalled once for repeated crkv_quantize_q8 calls."""
+
+    def __init__(self, segs: Sequence[tuple]):
+        self.n = len(segs)
+        self.arr = (crkv_q8_seg * self.n)(*[crkv_q8_seg(_ptr(x), _ptr(q), int(n), int(k))
+                                            for x, q, n, k in segs])
+
+
+def crkv_quantize_q8(segs, H_kv: int, d: int, stream=None, timing_events=None):
+    """Quantise bf16 segments into the 8-bit format: segs is a list of
+    (x bf16 tensor [H_kv][len][d], q8 uint8 tensor of crkv_q8_bytes bytes, len,
+    kind CRKV_Q8_K or CRKV_Q8_V), or a Q8Batch."""
+    b = segs if isinstance(segs, Q8Batch) else Q8Batch(segs)
+    o = make_opts(CRKV_BF16, "query", stream, timing_events=timing_events)
+    _check(lib().crkv_quantize_q8(b.arr, b.n, H_kv, d, ctypes.byref(o)))
 
 
 def crkv_budget(n_doc: int, r: float) -> int:

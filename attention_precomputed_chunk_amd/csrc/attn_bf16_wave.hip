@@ -133,9 +133,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             const float tmax = fmaxf(fmaxf(fmaxf(row_m[rt], s0[0]), fmaxf(s0[1], s0[2])),
                                      fmaxf(fmaxf(s0[3], s1[0]), fmaxf(fmaxf(s1[1], s1[2]), s1[3])));
             const float mc = ((tmax == -INFINITY) ? 0.f : tmax) * c;
-            float sum = 0.f;
+            float sum = exp2_hw(__builtin_fmaf(s0[0], c, -mc)) + exp2_hw(__builtin_fmaf(s1[0], c, -mc));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 1; e < 4; ++e)
                 sum += exp2_hw(__builtin_fmaf(s0[e], c, -mc)) + exp2_hw(__builtin_fmaf(s1[e], c, -mc));
             row_l[rt] = __builtin_fmaf(row_l[rt], exp2_hw(__builtin_fmaf(row_m[rt], c, -mc)), sum);
             row_m[rt] = tmax;
@@ -163,13 +163,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[rt][ks], s1, 0, 0, 0);
             }
             const float mc = row_m[rt] * c;
-            float a = 0.f, b = 0.f;
+            float e[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a += exp2_hw(__builtin_fmaf(s0[e], c, -mc));
-                b += exp2_hw(__builtin_fmaf(s1[e], c, -mc));
+            for (int i = 0; i < 4; ++i) {
+                e[i] = exp2_hw(__builtin_fmaf(s0[i], c, -mc));
+                e[4 + i] = exp2_hw(__builtin_fmaf(s1[i], c, -mc));
             }
-            sum[rt] = a + b;
+            sum[rt] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
             big |= sum[rt] > kLseRescaleBound;
         }
         if (__builtin_amdgcn_ballot_w64(big))
@@ -255,9 +255,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         }
         float imp[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            imp[i] = 0.f;
-#pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -286,11 +283,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                 const float w = (row_pos[rt] >= kt.seg_lo && row_pos[rt] < kt.seg_lo + kt.seg_len) ? 0.f : 1.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    imp[i] = __builtin_fmaf(p[i], w, imp[i]);
+                    imp[i] = rt == 0 ? p[i] * w : __builtin_fmaf(p[i], w, imp[i]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    imp[i] += p[i];
+                    imp[i] = rt == 0 ? p[i] : imp[i] + p[i];
             }
             bf16x8 pb;
 #pragma unroll
@@ -331,9 +328,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
         float imp[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            imp[i] = 0.f;
         f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -367,11 +361,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                 const float w = (row_pos[rt] >= kt.seg_lo && row_pos[rt] < kt.seg_lo + kt.seg_len) ? 0.f : 1.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    imp[i] = __builtin_fmaf(p[i], w, imp[i]);
+                    imp[i] = rt == 0 ? p[i] * w : __builtin_fmaf(p[i], w, imp[i]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    imp[i] += p[i];
+                    imp[i] = rt == 0 ? p[i] : imp[i] + p[i];
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)

@@ -36,6 +36,9 @@ hipError_t launch_topk_batched(const TopkDesc *descs, int n, hipStream_t stream)
 hipError_t launch_topk_inline(const TopkDesc *descs, int n, hipStream_t stream);
 hipError_t launch_kvsel(bool scatter, const SelArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_rope_shift(int d, bool bf16, const RopeArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_quantize_q8(int d, const Q8Args &v_args, int n_v, const Q8Args &k_args, int n_k,
+                              hipStream_t stream);
+hipError_t launch_decode_q8(int d, const DecodeArgs &args, int n_items, int n_pairs, hipStream_t stream);
 }  // namespace crkv
 
 using namespace crkv;
@@ -682,11 +685,13 @@ struct DecodePlan {
 int validate_decode(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                     const crkv_opts &o)
 {
-    int rc = check_opts(o);
+    if (o.dtype != CRKV_BF16 && o.dtype != CRKV_KV_Q8)
+        return fail(CRKV_E_UNSUPPORTED, "decode: opts.dtype %d (only CRKV_BF16 and CRKV_KV_Q8)", o.dtype);
+    crkv_opts ob = o;   // the remaining options are checked as for bf16
+    ob.dtype = CRKV_BF16;
+    int rc = check_opts(ob);
     if (rc)
         return rc;
-    if (o.dtype != CRKV_BF16)
-        return fail(CRKV_E_UNSUPPORTED, "decode: only CRKV_BF16 is supported");
     rc = check_shape(n_problems, H, H_kv, d);
     if (rc)
         return rc;
@@ -729,14 +734,14 @@ void append_tiles(std::vector<KTile> &tiles, const crkv_problem &p, int d, size_
 // `split` chosen so that the launch has about kDecodeTargetItems workgroups
 // (a multiple of the split kernel's 4 waves, at least 4 tiles, at most 256).
 void build_decode_plan(DecodePlan &pl, const crkv_problem *problems, int n_problems, int H, int H_kv,
-                       int d)
+                       int d, size_t esz)
 {
     const int G = H / H_kv;
     int64_t all_tiles = 0;
     pl.probs.resize(n_problems);
     for (int pi = 0; pi < n_problems; ++pi) {
         pl.tile_base.push_back(pl.tiles.size());
-        append_tiles(pl.tiles, problems[pi], d, 2);
+        append_tiles(pl.tiles, problems[pi], d, esz);
         all_tiles += (int64_t)(pl.tiles.size() - pl.tile_base.back()) * H_kv;
     }
     int64_t split = (all_tiles + kDecodeTargetItems - 1) / kDecodeTargetItems;
@@ -986,7 +991,110 @@ int run_rope(const crkv_rope_seg *segs, int n, int H_kv, int d, double base, con
     return e == hipSuccess ? CRKV_OK : hip_fail(e, "key re-positioning launch");
 }
 
+// ------------------------------------------------------------ 8-bit segments
+size_t q8_bytes(int H_kv, int len, int d, int kind)
+{
+    if (H_kv < 0 || len < 0 || (d != 64 && d != 128) || (kind != CRKV_Q8_K && kind != CRKV_Q8_V))
+        return 0;
+    if (len == 0)
+        return 0;
+    return (size_t)H_kv * len * d + (size_t)H_kv * (kind == CRKV_Q8_K ? d : len) * sizeof(float);
+}
+
+int run_quantize(const crkv_q8_seg *segs, int n, int H_kv, int d, const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = check_opts(o);
+    if (rc)
+        return rc;
+    if (o.dtype != CRKV_BF16)
+        return fail(CRKV_E_UNSUPPORTED, "quantize: the input must be CRKV_BF16");
+    if (n < 1 || !segs)
+        return fail(CRKV_E_INVAL, "n = %d segments (need >= 1, non-null array)", n);
+    if (H_kv < 1)
+        return fail(CRKV_E_INVAL, "H_kv = %d < 1", H_kv);
+    if (d != 64 && d != 128)
+        return fail(CRKV_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", d);
+    for (int i = 0; i < n; ++i) {
+        if (segs[i].len < 0)
+            return fail(CRKV_E_INVAL, "segment %d: len = %d < 0", i, segs[i].len);
+        if ((int64_t)segs[i].len * H_kv >= (int64_t(1) << 31))
+            return fail(CRKV_E_UNSUPPORTED, "segment %d: %lld rows (limit 2^31)", i,
+                        (long long)segs[i].len * H_kv);
+        if (segs[i].kind != CRKV_Q8_K && segs[i].kind != CRKV_Q8_V)
+            return fail(CRKV_E_INVAL, "segment %d: kind %d is not CRKV_Q8_K or CRKV_Q8_V", i, segs[i].kind);
+        if (segs[i].len == 0)
+            continue;
+        if (!segs[i].x || !segs[i].q8 || !aligned16(segs[i].x) || !aligned16(segs[i].q8))
+            return fail(CRKV_E_INVAL, "segment %d: x and q8 must be non-null and 16-byte aligned", i);
+        const uintptr_t x0 = reinterpret_cast<uintptr_t>(segs[i].x);
+        const uintptr_t q0 = reinterpret_cast<uintptr_t>(segs[i].q8);
+        const size_t xb = (size_t)H_kv * segs[i].len * d * 2, qb = q8_bytes(H_kv, segs[i].len, d, segs[i].kind);
+        if (x0 < q0 + qb && q0 < x0 + xb)
+            return fail(CRKV_E_INVAL, "segment %d: q8 overlaps x", i);
+    }
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    std::vector<Q8Seg> qs;
+    std::vector<Q8Item> v_items, k_items;   // V: blocks of rows; K: one per (segment, KV head)
+    for (int i = 0; i < n; ++i) {
+        if (segs[i].len == 0)
+            continue;
+        Q8Seg q{};
+        q.x = segs[i].x;
+        q.q8 = segs[i].q8;
+        q.rows = segs[i].len * H_kv;
+        q.len = segs[i].len;
+        const int idx = (int)qs.size();
+        qs.push_back(q);
+        if (segs[i].kind == CRKV_Q8_V) {
+            for (int r0 = 0; r0 < q.rows; r0 += kQ8RowsPerItem)
+                v_items.push_back(Q8Item{idx, r0});
+        } else {
+            for (int h = 0; h < H_kv; ++h)
+                k_items.push_back(Q8Item{idx, h});
+        }
+    }
+    if (qs.empty())
+        return CRKV_OK;
+    std::vector<Q8Item> items(v_items);
+    items.insert(items.end(), k_items.begin(), k_items.end());
+    const size_t off_items = align_up(qs.size() * sizeof(Q8Seg), 256);
+    const size_t bytes = align_up(off_items + items.size() * sizeof(Q8Item), 256);
+    PlanLease lease;
+    rc = plan_acquire(lease, bytes);
+    if (rc)
+        return rc;
+    memset(lease.host, 0, bytes);
+    memcpy(lease.host, qs.data(), qs.size() * sizeof(Q8Seg));
+    memcpy(lease.host + off_items, items.data(), items.size() * sizeof(Q8Item));
+    rc = plan_commit(lease, bytes, stream);
+    hipError_t e = hipSuccess;
+    if (rc == CRKV_OK) {
+        Q8Args va{}, ka{};
+        va.segs = ka.segs = reinterpret_cast<const Q8Seg *>(lease.dev);
+        va.items = reinterpret_cast<const Q8Item *>(lease.dev + off_items);
+        ka.items = va.items + v_items.size();
+        if (o.timing_events[0])
+            e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
+        if (e == hipSuccess)
+            e = launch_quantize_q8(d, va, (int)v_items.size(), ka, (int)k_items.size(), stream);
+        if (e == hipSuccess && o.timing_events[1])
+            e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    }
+    plan_release(lease, stream);
+    if (rc)
+        return rc;
+    return e == hipSuccess ? CRKV_OK : hip_fail(e, "quantize launch");
+}
+
 extern "C" {
+
+size_t crkv_q8_bytes(int H_kv, int len, int d, int kind) { return q8_bytes(H_kv, len, d, kind); }
+
+int crkv_quantize_q8(const crkv_q8_seg *segs, int n, int H_kv, int d, const crkv_opts *opts)
+{
+    return run_quantize(segs, n, H_kv, d, opts);
+}
 
 void crkv_opts_init(crkv_opts *opts)
 {
@@ -1008,7 +1116,7 @@ size_t crkv_decode_workspace_size(const crkv_problem *problems, int n_problems, 
     if (validate_decode(problems, n_problems, H, H_kv, d, o) != CRKV_OK)
         return 0;
     DecodePlan pl;
-    build_decode_plan(pl, problems, n_problems, H, H_kv, d);
+    build_decode_plan(pl, problems, n_problems, H, H_kv, d, o.dtype == CRKV_KV_Q8 ? 1 : 2);
     return pl.scratch_bytes;
 }
 
@@ -1021,7 +1129,8 @@ int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int
         return rc;
     hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
     DecodePlan pl;
-    build_decode_plan(pl, problems, n_problems, H, H_kv, d);
+    const bool q8 = o.dtype == CRKV_KV_Q8;
+    build_decode_plan(pl, problems, n_problems, H, H_kv, d, q8 ? 1 : 2);
     Scratch sc;
     rc = scratch_get(sc, pl.scratch_bytes, o, stream);
     if (rc)
@@ -1058,11 +1167,13 @@ int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int
     args.part = static_cast<float *>(sc.ptr);
     args.G = H / H_kv;
     args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    args.H_kv = H_kv;
     hipError_t e = hipSuccess;
     if (o.timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
     if (e == hipSuccess)
-        e = launch_decode_bf16(d, args, (int)pl.items.size(), (int)pl.pairs.size(), stream);
+        e = q8 ? launch_decode_q8(d, args, (int)pl.items.size(), (int)pl.pairs.size(), stream)
+               : launch_decode_bf16(d, args, (int)pl.items.size(), (int)pl.pairs.size(), stream);
     if (e == hipSuccess && o.timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
     plan_release(lease, stream);

@@ -117,6 +117,8 @@ struct DecodeArgs {
     float *part;            // per slot: G x (max, sum) then G x d unnormalised output
     int32_t G;
     float c_log2;           // log2(e) / sqrt(d)
+    int32_t H_kv;           // 8-bit segments: the scales follow H_kv * len * d code bytes
+    int32_t pad;
 };
 
 struct TopkDesc {
@@ -190,5 +192,31 @@ struct RopeArgs {
     int32_t bf16;
 };
 static_assert(sizeof(RopeSeg) == 24 && sizeof(RopeItem) == 8, "table layout");
+
+// ---------------------------------------------------------------- 8-bit K/V segments
+// A segment [H_kv][len][d] in the 8-bit format is one buffer: int8 codes
+// [H_kv][len][d], then float32 scales (value = code * scale): [H_kv][d], one
+// per channel over the segment's tokens, for K; [H_kv][len], one per token,
+// for V.
+constexpr int kQ8Threads = 256;
+constexpr int kQ8RowsPerItem = 256;     // V: rows ([H_kv * len] of a segment) per workgroup
+
+struct Q8Seg {
+    const void *x;            // bf16 [H_kv][len][d]
+    void *q8;                 // codes, then scales
+    int32_t rows;             // H_kv * len
+    int32_t len;
+};
+
+struct Q8Item {
+    int32_t seg;
+    int32_t row0;             // V: first row of the workgroup; K: the KV head
+};
+
+struct Q8Args {
+    const Q8Seg *segs;
+    const Q8Item *items;
+};
+static_assert(sizeof(Q8Seg) == 24 && sizeof(Q8Item) == 8, "table layout");
 
 }  // namespace crkv

@@ -274,6 +274,18 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeArgs a)
     }
 }
 
+// The merge alone (also used after the split step over 8-bit segments).
+hipError_t launch_decode_merge(int d, const DecodeArgs &args, int n_pairs, hipStream_t stream)
+{
+    if (n_pairs <= 0)
+        return hipSuccess;
+    if (d == 128)
+        hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(n_pairs), dim3(256), 0, stream, args);
+    else
+        hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(n_pairs), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_bf16(int d, const DecodeArgs &args, int n_items, int n_pairs, hipStream_t stream)
 {
     if (n_items <= 0)

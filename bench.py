@@ -19,6 +19,11 @@ layer's selected keys (the top-1500 of the default workload's impact, found
 once before timing): one gather launch into packed buffers and one scatter
 launch back into the segments.
 
+With --config llama3_8b_decode_q8_32l a step is the same decode step over the
+cache stored in the 8-bit format (codes + one float32 scale per row; the
+cache is quantised once before timing, as it is when the chunk caches are
+precomputed).
+
 With --config llama3_8b_rope_shift_32l a step moves the cached keys of every
 document chunk of the 32 layers from positions 0 .. 2499 to their place in the
 concatenation (offsets 2500, 5000, 7500; the first chunk stays): one
@@ -48,6 +53,7 @@ METRIC_SELECT = "selected token-layers/s through K/V gather + scatter; % of HBM 
 SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
 METRIC_ROPE = "re-positioned key-layers/s (rotary shift of cached keys); % of HBM roofline"
 ROPE_CONFIGS = {"llama3_8b_rope_shift_32l": "llama3_8b_gqa_32l"}
+Q8_CONFIGS = {"llama3_8b_decode_q8_32l": "llama3_8b_decode_32l"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -85,6 +91,8 @@ KERNEL_SOURCES = {
     "decode": ("decode_bf16.hip", "attn_bf16_common.h", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
     "kvsel": ("kvsel.hip", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
     "rope": ("rope.hip", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
+    "q8": ("q8.hip", "decode_bf16.hip", "attn_bf16_common.h", "device_util.h", "crkv_internal.h",
+           "crkv_api.hip"),
 }
 
 
@@ -155,6 +163,100 @@ def cpu_baseline(wl, budget_s=15.0):
     return {"value": tokens / elapsed, "unit": "KV tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle", "sample": "problems 0..%d of %d (%s), %.1f s of CPU time"
             % (n - 1, len(wl.problems), wl.spec.name if wl.spec else "custom", elapsed)}
+
+
+def bench_q8_decode(args, torch, crkv, workloads):
+    """One decode step over the 8-bit cache (all layers, one launch of the
+    split kernel and one of the merge); the roofline is the pair's."""
+    from_cfg = Q8_CONFIGS[args.config]
+    log("generating %s" % from_cfg)
+    wl = workloads.generate(from_cfg)
+    dev = "cuda:0"
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    problems, segs, keep = [], [], []
+    q8_bytes = 0
+    for p in wl.problems:
+        Q = up(p.Q)
+        kq, vq = [], []
+        for k, v, n in zip(p.K, p.V, p.lens):
+            nk = crkv.crkv_q8_bytes(wl.H_kv, n, wl.d, crkv.CRKV_Q8_K)
+            nv = crkv.crkv_q8_bytes(wl.H_kv, n, wl.d, crkv.CRKV_Q8_V)
+            q8_bytes += nk + nv
+            bk = torch.empty(max(nk, 16), dtype=torch.uint8, device=dev)
+            bv = torch.empty(max(nv, 16), dtype=torch.uint8, device=dev)
+            kd, vd = up(k), up(v)
+            segs += [(kd, bk, n, crkv.CRKV_Q8_K), (vd, bv, n, crkv.CRKV_Q8_V)]
+            keep += [kd, vd]
+            kq.append(bk)
+            vq.append(bv)
+        problems.append(dict(Q=Q, chunk_K=kq, chunk_V=vq, chunk_len=list(p.lens), q_len=1,
+                             out=torch.empty_like(Q), impact=None))
+    qev = HipEvents()
+    qa, qb = qev.create(), qev.create()
+    crkv.crkv_quantize_q8(segs, wl.H_kv, wl.d, timing_events=(qa, qb))   # once: the stored cache
+    torch.cuda.synchronize()
+    q_ms = qev.elapsed_ms(qa, qb)
+    del segs, keep
+    torch.cuda.empty_cache()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    batch = crkv.Batch(problems)
+
+    def step(events=None):
+        crkv.crkv_decode_chunks_batched(batch, wl.H, wl.H_kv, wl.d, timing_events=events,
+                                        dtype=crkv.CRKV_KV_Q8)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    tokens = workloads.kv_tokens(wl)
+    # algorithmic bytes: every key's K and V codes and scales once, Q and out (bf16)
+    nbytes = q8_bytes + sum(2 * wl.H * wl.d * 2 for _ in wl.problems)
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    spec = wl.spec
+    cfg = {"workload": args.config, "problems": len(wl.problems), "H": wl.H, "H_kv": wl.H_kv, "d": wl.d,
+           "chunks": len(spec.chunk_lens), "chunk_len": spec.chunk_lens[0], "n_doc": int(sum(spec.chunk_lens)),
+           "gen_len": spec.gen_len, "q_len": 1, "step": "decode", "kv_format": "int8 codes; fp32 scales per (KV head, channel) for K, per (KV head, token) for V"}
+    rec = {"metric": METRIC_DECODE, "value": round(tokens / (wall / args.steps), 1), "unit": "KV tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int8 (K/V), bf16 (Q, out), f32 accumulate", "data": "synthetic",
+           "config": cfg,
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config, "q8"),
+                        "kernel": "decode_q8_split+merge", "kernel_ms": round(k_ms, 4),
+                        "alg_bytes_per_launch": nbytes},
+           "quantize_once": {"kernel": "quantize_q8_kernel", "ms": round(q_ms, 4),
+                             "bytes": int(sum(k.size + v.size for p in wl.problems for k, v in zip(p.K, p.V))) * 2 + q8_bytes},
+           "kv_tokens_per_step": tokens}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        from oracle import q8
+        t0 = time.perf_counter()
+        done = 0
+        for p in wl.problems:
+            q8.decode(p, wl.H, wl.H_kv, wl.d)
+            done += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        el = time.perf_counter() - t0
+        import oracle
+        rec["cpu_baseline"] = {"value": sum(p.n_keys for p in wl.problems[:done]) / el, "unit": "KV tokens/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": "layers 0..%d of %d (quantise + dequantise + fp64 decode), %.1f s"
+                               % (done - 1, len(wl.problems), el)}
+    print(json.dumps(rec), flush=True)
 
 
 def bench_select(args, torch, crkv, workloads):
@@ -346,6 +448,9 @@ def main():
         return
     if args.config in ROPE_CONFIGS:
         bench_rope(args, torch, crkv, workloads)
+        return
+    if args.config in Q8_CONFIGS:
+        bench_q8_decode(args, torch, crkv, workloads)
         return
 
     log("generating %s" % args.config)

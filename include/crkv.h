@@ -62,7 +62,10 @@ typedef enum {
     CRKV_E_NOMEM = -4        /* device or pinned host allocation failed      */
 } crkv_status;
 
-typedef enum { CRKV_F32 = 0, CRKV_BF16 = 1 } crkv_dtype;
+/* CRKV_KV_Q8: K/V segments in the 8-bit format of crkv_quantize_q8, Q and
+ * out bf16; accepted by crkv_decode_chunks_batched (and its workspace size)
+ * only, every other entry point returns CRKV_E_UNSUPPORTED or CRKV_E_INVAL. */
+typedef enum { CRKV_F32 = 0, CRKV_BF16 = 1, CRKV_KV_Q8 = 2 } crkv_dtype;
 
 /*
  * Which rows are attended and which rows count towards impact.
@@ -166,7 +169,14 @@ size_t crkv_workspace_size(const crkv_problem *problems, int n_problems, int H, 
  * the current one, whose query row (the last position) sees every key.
  * Computes out only: the problems' impact pointers are ignored (may be NULL).
  *  Q    device, [H][1][d]; out device, [H][1][d], written
- *  Requires opts->dtype == CRKV_BF16 (else CRKV_E_UNSUPPORTED) and
+ *  opts->dtype == CRKV_BF16: segments bf16 [H_kv][len][d]. opts->dtype ==
+ *  CRKV_KV_Q8: chunk_K[c] and chunk_V[c] are buffers in the 8-bit format of
+ *  crkv_quantize_q8 (kinds CRKV_Q8_K and CRKV_Q8_V, 16-byte aligned) for
+ *  chunk_len[c] keys; the step is the decode over the dequantised cache
+ *  (code * scale), with the scales applied outside the matrix products (Q
+ *  times the segment's K channel scales, rounded to bf16 once per segment;
+ *  softmax weight times the key's V scale before P.V); Q and out bf16.
+ *  Requires opts->dtype CRKV_BF16 or CRKV_KV_Q8 (else CRKV_E_UNSUPPORTED) and
  *  H / H_kv <= 16. opts->mode is ignored. The keys of each (problem, KV head)
  *  are split into ranges processed in parallel and merged in range order, so
  *  results are deterministic. Scratch: opts->workspace of at least
@@ -180,6 +190,43 @@ int crkv_decode_chunks_batched(const crkv_problem *problems, int n_problems, int
  * arguments (256-byte aligned workspace). Returns 0 if they are invalid. */
 size_t crkv_decode_workspace_size(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                                   const crkv_opts *opts);
+
+/*
+ * The 8-bit K/V segment format (CacheGen summary: loading a precomputed
+ * cache dominates, and caches can be stored in a much smaller form; the page
+ * gives no codec, so this format is this library's own). bf16 values become
+ * int8 codes with float32 scales, one scale per group, with float32 IEEE
+ * divisions and round-half-to-even:
+ *   scale = max over the group of |x| / 127,   code = clamp(rint(x / scale), -127, 127)
+ * (an all-zero group: scale 0, codes 0). Value = code * scale. K groups are
+ * (KV head, channel) over the segment's tokens, because cached keys carry a
+ * few large-magnitude channels; V groups are (KV head, token). A segment of
+ * len keys is one buffer of crkv_q8_bytes(H_kv, len, d, kind) bytes: the
+ * codes [H_kv][len][d] (int8), then at byte offset H_kv * len * d the scales,
+ * float32 [H_kv][d] (K) or [H_kv][len] (V). At d = 128 and 2,500 keys a K/V
+ * pair is 0.51x the bf16 bytes, and the decode step (CRKV_KV_Q8) reads that.
+ * K scales cover the tokens present when the segment was quantised: a
+ * segment that grows (the generated tokens' segment) is quantised again.
+ */
+typedef enum { CRKV_Q8_K = 0, CRKV_Q8_V = 1 } crkv_q8_kind;
+
+typedef struct crkv_q8_seg {
+    const void *x;   /* device bf16 [H_kv][len][d], read; 16-byte aligned       */
+    void *q8;        /* device, crkv_q8_bytes(H_kv, len, d, kind) bytes, written;
+                        16-byte aligned; must not overlap x                     */
+    int len;         /* >= 0 (0: nothing is written)                            */
+    int kind;        /* crkv_q8_kind: the segment holds keys or values          */
+} crkv_q8_seg;
+
+/* Bytes of one segment in the 8-bit format (0 for len = 0); 0 if an argument
+ * is negative, d is not 64 or 128, or kind is not a crkv_q8_kind. */
+size_t crkv_q8_bytes(int H_kv, int len, int d, int kind);
+
+/* Quantises n segments (K and V kinds mixed) in one call: one launch per
+ * kind present. Requires opts->dtype == CRKV_BF16 (the input type), H_kv >= 1,
+ * d in {64, 128}, H_kv * len < 2^31. opts->mode is ignored;
+ * opts->timing_events bracket the launches. */
+int crkv_quantize_q8(const crkv_q8_seg *segs, int n, int H_kv, int d, const crkv_opts *opts);
 
 /* The launch configuration crkv_attn_chunks_batched would use for these
  * arguments: *kernel = 0 for the fp32 kernel, 1 for the bf16 kernel with one

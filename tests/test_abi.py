@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(crkv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(crkv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(crkv_lib):
@@ -240,3 +240,47 @@ def test_rope_shift_rejects_invalid_arguments(crkv_lib):
     # nothing moves: delta 0, or an empty segment (valid; nothing is enqueued)
     idle = (crkv.crkv_rope_seg * 2)(crkv.crkv_rope_seg(None, 16, 0), crkv.crkv_rope_seg(None, 0, 7))
     assert L.crkv_rope_shift(idle, 2, 2, 128, 10000.0, ctypes.byref(o)) == 0
+
+
+def test_quantize_q8_rejects_invalid_arguments(crkv_lib):
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    o.dtype = crkv.CRKV_BF16
+    L = crkv_lib
+    q_at = FAKE + (1 << 20)
+    K, V = crkv.CRKV_Q8_K, crkv.CRKV_Q8_V
+    ok = (crkv.crkv_q8_seg * 2)(crkv.crkv_q8_seg(FAKE, q_at, 16, K), crkv.crkv_q8_seg(FAKE, q_at + 4096, 16, V))
+    assert L.crkv_quantize_q8(ok, 2, 2, 96, ctypes.byref(o)) == -2       # d
+    assert L.crkv_quantize_q8(ok, 2, 0, 128, ctypes.byref(o)) == -1      # H_kv
+    assert L.crkv_quantize_q8(ok, 0, 2, 128, ctypes.byref(o)) == -1      # n
+    for seg in (crkv.crkv_q8_seg(FAKE, q_at, -1, V), crkv.crkv_q8_seg(None, q_at, 16, V),
+                crkv.crkv_q8_seg(FAKE, None, 16, K), crkv.crkv_q8_seg(FAKE + 8, q_at, 16, K),
+                crkv.crkv_q8_seg(FAKE, q_at + 4, 16, V), crkv.crkv_q8_seg(FAKE, FAKE + 256, 16, K),
+                crkv.crkv_q8_seg(FAKE, q_at, 16, 2)):
+        bad = (crkv.crkv_q8_seg * 1)(seg)
+        assert L.crkv_quantize_q8(bad, 1, 2, 128, ctypes.byref(o)) == -1
+    for dt in (crkv.CRKV_F32, crkv.CRKV_KV_Q8):   # the input is bf16
+        o.dtype = dt
+        assert L.crkv_quantize_q8(ok, 2, 2, 128, ctypes.byref(o)) in (-1, -2)
+    o.dtype = crkv.CRKV_BF16
+    idle = (crkv.crkv_q8_seg * 2)(crkv.crkv_q8_seg(None, None, 0, K), crkv.crkv_q8_seg(None, None, 0, V))
+    assert L.crkv_quantize_q8(idle, 2, 2, 128, ctypes.byref(o)) == 0   # nothing to do
+    assert L.crkv_q8_bytes(8, 2500, 128, V) == 8 * 2500 * 128 + 4 * 8 * 2500
+    assert L.crkv_q8_bytes(8, 2500, 128, K) == 8 * 2500 * 128 + 4 * 8 * 128
+    assert L.crkv_q8_bytes(8, 0, 128, K) == 0
+    assert L.crkv_q8_bytes(8, 2500, 96, K) == 0 and L.crkv_q8_bytes(-1, 5, 64, V) == 0
+    assert L.crkv_q8_bytes(8, 5, 64, 7) == 0
+
+
+def test_q8_dtype_is_decode_only(crkv_lib):
+    """CRKV_KV_Q8 passes the decode step's validation (the workspace size is
+    computed) and is refused by the prefill entry points."""
+    p = dict(Q=FAKE, chunk_K=[FAKE, FAKE], chunk_V=[FAKE, FAKE], chunk_len=[64, 3], q_len=1,
+             out=FAKE, impact=FAKE)
+    assert crkv.crkv_decode_workspace_size([p], 8, 2, 128, dtype=crkv.CRKV_KV_Q8) > 0
+    with pytest.raises(crkv.CrkvError) as e:
+        crkv.crkv_attn_chunks_batched([p], 8, 2, 128, dtype=crkv.CRKV_KV_Q8)
+    assert e.value.status == -1
+    with pytest.raises(crkv.CrkvError) as e:
+        crkv.crkv_decode_chunks_batched([p], 8, 2, 128, dtype=5)
+    assert e.value.status == -2

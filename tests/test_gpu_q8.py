@@ -1,0 +1,197 @@
+"""GPU parity of the 8-bit K/V segment format through the C ABI: the
+quantisation is bit-exact against the oracle (codes and scales), and the
+decode step over quantised segments matches the oracle's fp64 decode over the
+dequantised cache within the bf16 bound."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import attention_precomputed_chunk_amd as crkv  # noqa: E402
+from oracle import q8  # noqa: E402
+import workloads  # noqa: E402
+from gpu_util import DEV, DeviceWorkload, check_out, to_host  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(crkv_lib):
+    yield
+
+
+class Q8Workload:
+    """A bf16 workload on the device plus its segments quantised by the
+    library (one launch over every K and V segment of every problem)."""
+
+    def __init__(self, wl, problems=None):
+        self.wl = wl
+        self.dw = DeviceWorkload(wl)
+        self.sel = range(len(wl.problems)) if problems is None else problems
+        segs = []
+        self.q = []
+        for pi in range(len(wl.problems)):
+            p = wl.problems[pi]
+            dp = self.dw.problems[pi]
+            kq, vq = [], []
+            for c, n in enumerate(p.lens):
+                nk = crkv.crkv_q8_bytes(wl.H_kv, n, wl.d, crkv.CRKV_Q8_K)
+                nv = crkv.crkv_q8_bytes(wl.H_kv, n, wl.d, crkv.CRKV_Q8_V)
+                bk = torch.full((max(nk, 16),), 0xA5, dtype=torch.uint8, device=DEV)
+                bv = torch.full((max(nv, 16),), 0x5A, dtype=torch.uint8, device=DEV)
+                segs.append((dp["chunk_K"][c], bk, n, crkv.CRKV_Q8_K))
+                segs.append((dp["chunk_V"][c], bv, n, crkv.CRKV_Q8_V))
+                kq.append(bk)
+                vq.append(bv)
+            self.q.append((kq, vq))
+        crkv.crkv_quantize_q8(segs, wl.H_kv, wl.d)
+        torch.cuda.synchronize()
+        self.problems = []
+        for pi, dp in enumerate(self.dw.problems):
+            kq, vq = self.q[pi]
+            self.problems.append(dict(Q=dp["Q"], chunk_K=kq, chunk_V=vq, chunk_len=dp["chunk_len"],
+                                      q_len=1, out=torch.empty_like(dp["Q"]), impact=None))
+
+    def host_segments(self, pi):
+        """(codes, scales) of every K and V segment of problem pi, read back."""
+        p = self.wl.problems[pi]
+        kq, vq = self.q[pi]
+        out = []
+        for bufs, kind, code in ((kq, "k", crkv.CRKV_Q8_K), (vq, "v", crkv.CRKV_Q8_V)):
+            segs = []
+            for c, n in enumerate(p.lens):
+                nb = crkv.crkv_q8_bytes(self.wl.H_kv, n, self.wl.d, code)
+                segs.append(q8.unpack(bufs[c][:nb].cpu().numpy(), self.wl.H_kv, n, self.wl.d, kind))
+            out.append(segs)
+        return out
+
+    def decode(self, **kw):
+        crkv.crkv_decode_chunks_batched(self.problems, self.wl.H, self.wl.H_kv, self.wl.d,
+                                        dtype=crkv.CRKV_KV_Q8, **kw)
+
+
+def check_codes(qw, pi):
+    p = qw.wl.problems[pi]
+    got_k, got_v = qw.host_segments(pi)
+    ref_k, ref_v = q8.quantize_problem(p)
+    for name, got, ref in (("K", got_k, ref_k), ("V", got_v, ref_v)):
+        for c, ((gc, gs), (rc, rs)) in enumerate(zip(got, ref)):
+            assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), \
+                "problem %d %s segment %d: scales differ" % (pi, name, c)
+            bad = np.argwhere(gc != rc)
+            assert bad.size == 0, "problem %d %s segment %d: %d codes differ, first at %s (%d vs %d)" % (
+                pi, name, c, len(bad), tuple(bad[0]), gc[tuple(bad[0])], rc[tuple(bad[0])])
+    return ref_k, ref_v
+
+
+def compare_decode(qw, problems=None, label=""):
+    wl = qw.wl
+    worst = 0.0
+    for pi in (range(len(wl.problems)) if problems is None else problems):
+        kq, vq = check_codes(qw, pi)
+        ref = q8.decode(wl.problems[pi], wl.H, wl.H_kv, wl.d, kq, vq)
+        worst = max(worst, check_out(to_host(qw.problems[pi]["out"]), ref, "bf16",
+                                     "%s[problem %d]" % (label, pi)))
+    return worst
+
+
+CASES = [
+    # seed, doc_lens, gen_len, H, H_kv, d, outlier channels
+    (1, [130, 67, 0, 5], 9, 8, 2, 128, 4),
+    (2, [64, 64], 0, 4, 4, 64, 0),
+    (3, [200, 1, 63], 100, 4, 1, 128, 4),
+    (4, [], 45, 16, 1, 128, 0),
+    (5, [511, 2], 300, 8, 8, 128, 4),
+    (6, [65, 0, 130], 31, 16, 2, 64, 4),
+    (7, [2048, 1000], 33, 8, 1, 128, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_q8_quantize_and_decode(case):
+    seed, doc, gen, H, H_kv, d, ko = CASES[case]
+    say("q8 case", CASES[case])
+    wl = workloads.custom(400 + seed, doc, 1, H, H_kv, d, dtype="bf16", n_problems=2, gen_len=gen,
+                          k_outliers=ko)
+    qw = Q8Workload(wl)
+    qw.decode()
+    torch.cuda.synchronize()
+    say("  out err %.3g" % compare_decode(qw, label="q8-%d" % case))
+
+
+def test_q8_edge_groups():
+    """Zero groups, a group whose float32 quotient is a tie (77 and 38.5: the
+    quotient is exactly 63.5 in float32, code 64), groups of tiny magnitude,
+    in both K (channels) and V (tokens), quantised bit-exactly; the decode
+    reads them."""
+    wl = workloads.custom(450, [40, 33], 1, 8, 2, 128, dtype="bf16", gen_len=10)
+    p = wl.problems[0]
+    tie = workloads.round_bf16(np.array([77.0, 38.5, -38.5, 1.0], dtype=np.float32))
+    k = p.K[0]
+    k[0, :, 5] = 0                                     # a zero channel
+    k[0, :, 6] = 0
+    k[0, :4, 6] = tie                                  # a channel with the tie
+    k[1, :, 9] = workloads.round_bf16(np.linspace(-1e-20, 1e-20, 40).astype(np.float32))
+    v = p.V[1]
+    v[0, 5, :] = 0                                     # a zero token
+    v[1, 2, :] = 0
+    v[1, 2, :4] = tie                                  # a token with the tie
+    qw = Q8Workload(wl)
+    (gk, gv) = qw.host_segments(0)
+    assert gk[0][1][0, 5] == 0 and not gk[0][0][0, :, 5].any()
+    assert gk[0][0][0, :4, 6].tolist() == [127, 64, -64, 2]
+    assert gv[1][1][0, 5] == 0 and not gv[1][0][0, 5].any()
+    assert gv[1][0][1, 2, :4].tolist() == [127, 64, -64, 2]
+    qw.decode()
+    torch.cuda.synchronize()
+    compare_decode(qw, label="q8-edge")
+
+
+def test_q8_decode_32_layers():
+    """The 32-layer decode workload quantised and decoded in one launch each:
+    codes of layers 0 and 31 bit-exact, their output against the oracle."""
+    say("llama3_8b_decode_32l (8-bit)")
+    wl = workloads.generate("llama3_8b_decode_32l")
+    qw = Q8Workload(wl)
+    qw.decode()
+    torch.cuda.synchronize()
+    say("  out err %.3g" % compare_decode(qw, problems=[0, 31], label="q8-32l"))
+
+
+def test_q8_decode_deterministic_and_workspace():
+    wl = workloads.custom(460, [700, 300], 1, 8, 2, 128, dtype="bf16", n_problems=2, gen_len=50)
+    qw = Q8Workload(wl)
+    qw.decode()
+    first = [p["out"].clone() for p in qw.problems]
+    nbytes = crkv.crkv_decode_workspace_size(qw.problems, wl.H, wl.H_kv, wl.d, dtype=crkv.CRKV_KV_Q8)
+    assert nbytes > 0
+    ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        qw.decode(workspace=ws, workspace_bytes=nbytes, stream=side)
+    side.synchronize()
+    for a, p in zip(first, qw.problems):
+        assert torch.equal(a, p["out"])
+
+
+def test_q8_error_against_the_bf16_cache():
+    """How far the 8-bit cache moves the decode output from the bf16 cache's
+    (the format's quantisation error, not a parity bound): reported, and
+    bounded loosely (on this layer the fp64 figure is 2.4 %)."""
+    wl = workloads.generate("llama3_8b_decode_32l", problems=[3])
+    qw = Q8Workload(wl)
+    qw.decode()
+    torch.cuda.synchronize()
+    import oracle
+    ref, _, _ = oracle.attn(wl.problems[0], wl.H, wl.H_kv, wl.d, "bf16", "query")
+    got = to_host(qw.problems[0]["out"])
+    rel = float((np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
+    say("  8-bit cache vs bf16 cache: row-relative max error %.3g" % rel)
+    assert rel < 0.05
