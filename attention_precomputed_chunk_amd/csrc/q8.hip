@@ -13,10 +13,12 @@
 // carry a few large-magnitude channels; V a group per (KV head, token).
 //
 // quantize_q8_token_kernel (V): one row per d/8 lanes (8 values per lane),
-// the row's maximum by lane shuffles, codes written as 8-byte pieces.
+// the row's maximum by lane shuffles, codes written as 8-byte pieces; a
+// thread issues the loads of all its rows before the first is used.
 // quantize_q8_channel_kernel (K): one workgroup per (segment, KV head); the
 // channel maxima over the tokens are reduced through LDS, then the tokens are
-// read a second time (from L2) and coded.
+// read a second time (from L2) and coded; four rows' loads in flight per
+// thread in both passes.
 //
 // decode_q8_split_kernel: the split step of the bf16 decode
 // (decode_bf16.hip) with 8-bit operands. The codes are small integers, exact
@@ -51,9 +53,19 @@ __global__ void __launch_bounds__(kQ8Threads) quantize_q8_token_kernel(const Q8A
     const gptr<u32x2> codes = as_global(static_cast<u32x2 *>(sg.q8));
     const gptr<float> scales = as_global(reinterpret_cast<float *>(static_cast<unsigned char *>(sg.q8) +
                                                                    (size_t)sg.rows * D));
+    constexpr int PER = kQ8RowsPerItem / RPP;   // rows per thread
     const int row_end = min(sg.rows, it.row0 + kQ8RowsPerItem);
-    for (int r = it.row0 + (int)threadIdx.x / LPR; r < row_end; r += RPP) {
-        const u32x4 v = x[(size_t)r * LPR + g];
+    const int r0 = it.row0 + (int)threadIdx.x / LPR;
+    u32x4 vs[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        vs[k] = r0 + k * RPP < row_end ? x[(size_t)(r0 + k * RPP) * LPR + g] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int r = r0 + k * RPP;
+        if (r >= row_end)   // the same for every lane of the row
+            break;
+        const u32x4 v = vs[k];
         float f[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -108,12 +120,20 @@ __global__ void __launch_bounds__(kQ8Threads) quantize_q8_channel_kernel(const Q
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         mx[e] = 0.f;
-    for (int r = rg; r < len; r += RG) {
-        float f[8];
-        widen(x[(size_t)r * LPR + g], f);
+    constexpr int UN = 4;                        // rows in flight per thread
+    for (int r0 = rg; r0 < len; r0 += UN * RG) {
+        u32x4 v[UN];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            mx[e] = fmaxf(mx[e], fabsf(f[e]));
+        for (int k = 0; k < UN; ++k)   // a missing row reads as zeros: no effect on a maximum
+            v[k] = r0 + k * RG < len ? x[(size_t)(r0 + k * RG) * LPR + g] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < UN; ++k) {
+            float f[8];
+            widen(v[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                mx[e] = fmaxf(mx[e], fabsf(f[e]));
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -133,16 +153,25 @@ __global__ void __launch_bounds__(kQ8Threads) quantize_q8_channel_kernel(const Q
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         s[e] = sc[8 * g + e];
-    for (int r = rg; r < len; r += RG) {
-        float f[8];
-        widen(x[(size_t)r * LPR + g], f);
-        uint32_t w[2] = {0u, 0u};
+    for (int r0 = rg; r0 < len; r0 += UN * RG) {
+        u32x4 v[UN];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float q = s[e] > 0.f ? fminf(fmaxf(__builtin_rintf(f[e] / s[e]), -127.f), 127.f) : 0.f;
-            w[e / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (e % 4));
+        for (int k = 0; k < UN; ++k)
+            v[k] = r0 + k * RG < len ? x[(size_t)(r0 + k * RG) * LPR + g] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < UN; ++k) {
+            if (r0 + k * RG >= len)
+                break;
+            float f[8];
+            widen(v[k], f);
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float q = s[e] > 0.f ? fminf(fmaxf(__builtin_rintf(f[e] / s[e]), -127.f), 127.f) : 0.f;
+                w[e / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (e % 4));
+            }
+            codes[(size_t)(r0 + k * RG) * LPR + g] = u32x2{w[0], w[1]};
         }
-        codes[(size_t)r * LPR + g] = u32x2{w[0], w[1]};
     }
 }
 

@@ -193,10 +193,12 @@ def bench_q8_decode(args, torch, crkv, workloads):
                              out=torch.empty_like(Q), impact=None))
     qev = HipEvents()
     qa, qb = qev.create(), qev.create()
-    crkv.crkv_quantize_q8(segs, wl.H_kv, wl.d, timing_events=(qa, qb))   # once: the stored cache
+    qbatch = crkv.Q8Batch(segs)
+    crkv.crkv_quantize_q8(qbatch, wl.H_kv, wl.d)   # the stored cache (the first launch also loads the code)
+    crkv.crkv_quantize_q8(qbatch, wl.H_kv, wl.d, timing_events=(qa, qb))   # the same again, timed
     torch.cuda.synchronize()
     q_ms = qev.elapsed_ms(qa, qb)
-    del segs, keep
+    del segs, keep, qbatch
     torch.cuda.empty_cache()
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
@@ -237,7 +239,7 @@ def bench_q8_decode(args, torch, crkv, workloads):
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config, "q8"),
                         "kernel": "decode_q8_split+merge", "kernel_ms": round(k_ms, 4),
                         "alg_bytes_per_launch": nbytes},
-           "quantize_once": {"kernel": "quantize_q8_kernel", "ms": round(q_ms, 4),
+           "quantize_once": {"kernels": "quantize_q8_token_kernel + quantize_q8_channel_kernel", "ms": round(q_ms, 4),
                              "bytes": int(sum(k.size + v.size for p in wl.problems for k, v in zip(p.K, p.V))) * 2 + q8_bytes},
            "kv_tokens_per_step": tokens}
     if not args.no_cpu_baseline:
