@@ -77,7 +77,7 @@ class crkv_q8_seg(ctypes.Structure):
 
 _lib = None
 
-DECLARED = ["crkv_q8_bytes", "crkv_quantize_q8", "crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
+DECLARED = ["crkv_plan_create", "crkv_plan_launch", "crkv_plan_destroy", "crkv_q8_bytes", "crkv_quantize_q8", "crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
             "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
             "crkv_decode_chunks_batched", "crkv_decode_workspace_size", "crkv_gather_kv",
             "crkv_scatter_kv", "crkv_rope_shift",
@@ -133,6 +133,14 @@ def lib():
         L.crkv_rope_shift.argtypes = [ctypes.POINTER(crkv_rope_seg), c_int, c_int, c_int, ctypes.c_double,
                                       ctypes.POINTER(crkv_opts)]
         L.crkv_rope_shift.restype = c_int
+        L.crkv_plan_create.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                       ctypes.POINTER(i32), ctypes.POINTER(vp), ctypes.POINTER(crkv_opts),
+                                       ctypes.POINTER(vp)]
+        L.crkv_plan_create.restype = c_int
+        L.crkv_plan_launch.argtypes = [vp, vp, ctypes.POINTER(vp)]
+        L.crkv_plan_launch.restype = c_int
+        L.crkv_plan_destroy.argtypes = [vp]
+        L.crkv_plan_destroy.restype = c_int
         L.crkv_q8_bytes.argtypes = [c_int, c_int, c_int, c_int]
         L.crkv_q8_bytes.restype = ctypes.c_size_t
         L.crkv_quantize_q8.argtypes = [ctypes.POINTER(crkv_q8_seg), c_int, c_int, c_int, ctypes.POINTER(crkv_opts)]
@@ -251,6 +259,54 @@ def crkv_attn_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int
     o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream,
                   workspace, workspace_bytes, timing_events)
     _check(lib().crkv_attn_chunks_batched(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+class Plan:
+    """A batched attention (+ top-k) call planned once (crkv_plan_create):
+    launch() only enqueues kernels, so it can be captured into a graph.
+    problems as for crkv_attn_chunks_batched; ks / idxs: per-problem top-k
+    budgets (0 = none) and int32 device tensors, or None for no selection."""
+
+    def __init__(self, problems: Sequence[dict], H: int, H_kv: int, d: int, ks: Optional[Sequence[int]] = None,
+                 idxs: Optional[Sequence] = None, mode: str = "query", dtype: Optional[int] = None,
+                 workspace=None, workspace_bytes: int = 0):
+        self._keep, self._arr = _problems(problems)
+        n = len(self._keep)
+        o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream=0, workspace=workspace,
+                      workspace_bytes=workspace_bytes)
+        self._workspace = workspace   # must outlive the plan
+        self._k = self._idx = None
+        if ks is not None:
+            self._k = (ctypes.c_int32 * n)(*[int(k) for k in ks])
+            self._idx = (ctypes.c_void_p * n)(*[_ptr(x) for x in idxs])
+        h = ctypes.c_void_p()
+        _check(lib().crkv_plan_create(self._arr, n, H, H_kv, d, self._k, self._idx, ctypes.byref(o),
+                                      ctypes.byref(h)))
+        self.handle = h.value
+
+    def launch(self, stream=None, timing_events=None):
+        if not self.handle:
+            raise ValueError("plan destroyed")
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
+        ev = None
+        if timing_events is not None:
+            ev = (ctypes.c_void_p * 2)(timing_events[0], timing_events[1])
+        _check(lib().crkv_plan_launch(self.handle, stream or None, ev))
+
+    def destroy(self):
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(lib().crkv_plan_destroy(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
 
 
 def crkv_workspace_size(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: str = "query",

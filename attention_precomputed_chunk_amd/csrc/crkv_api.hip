@@ -991,6 +991,154 @@ int run_rope(const crkv_rope_seg *segs, int n, int H_kv, int d, double base, con
     return e == hipSuccess ? CRKV_OK : hip_fail(e, "key re-positioning launch");
 }
 
+// ------------------------------------------------------------ prepared plans
+// A batched attention (and top-k) call planned once: its tables, impact
+// partials and top-k descriptors live in device memory owned by the plan, so
+// a launch only enqueues kernels (capturable in a hipGraph).
+struct crkv_plan {
+    int device = 0;
+    int n_problems = 0;
+    int d = 0;
+    int dtype = CRKV_F32;
+    int kernel = kBf16Wave, rt = 1, n_items = 0, max_keys = 0;
+    AttnArgs args{};
+    unsigned char *tables = nullptr;          // device plan tables
+    void *scratch = nullptr;                  // device impact partials
+    bool own_scratch = false;
+    std::vector<TopkDesc> topk;               // one per selecting problem (may be empty)
+    TopkDesc *topk_dev = nullptr;             // the same, on the device, past kTopkInline
+};
+
+void plan_free(crkv_plan *p)
+{
+    if (!p)
+        return;
+    if (p->tables)
+        (void)hipFree(p->tables);
+    if (p->own_scratch && p->scratch)
+        (void)hipFree(p->scratch);
+    if (p->topk_dev)
+        (void)hipFree(p->topk_dev);
+    delete p;
+}
+
+int plan_create(const crkv_problem *problems, int n_problems, int H, int H_kv, int d, const int32_t *k,
+                int32_t *const *idx, const crkv_opts *opts, crkv_plan **out)
+{
+    if (!out)
+        return fail(CRKV_E_INVAL, "plan output pointer must be non-null");
+    *out = nullptr;
+    const crkv_opts o = resolve(opts);
+    int rc = validate_batch(problems, n_problems, H, H_kv, d, o);
+    if (rc)
+        return rc;
+    std::vector<TopkDesc> descs;
+    if (k) {
+        if (!idx)
+            return fail(CRKV_E_INVAL, "k given without idx");
+        for (int i = 0; i < n_problems; ++i) {
+            int64_t n_doc = 0;
+            for (int c = 0; c < problems[i].m; ++c)
+                n_doc += problems[i].chunk_len[c];
+            if (k[i] == 0)
+                continue;   // this problem selects nothing
+            rc = check_topk_args(problems[i].impact, (int)n_doc, k[i], idx[i], i);
+            if (rc)
+                return rc;
+            descs.push_back(TopkDesc{problems[i].impact, idx[i], (int32_t)n_doc, k[i]});
+        }
+    }
+    Plan pl;
+    build_plan(pl, problems, n_problems, H, H_kv, d, o);
+    if (o.workspace && o.workspace_bytes < pl.scratch_bytes)
+        return fail(CRKV_E_INVAL, "workspace too small: %zu bytes given, %zu needed", o.workspace_bytes,
+                    pl.scratch_bytes);
+    std::unique_ptr<crkv_plan, void (*)(crkv_plan *)> p(new crkv_plan(), plan_free);
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    e = hipMalloc(reinterpret_cast<void **>(&p->tables), pl.table_bytes);
+    if (e != hipSuccess) {
+        p->tables = nullptr;
+        return hip_fail(e, "hipMalloc(plan tables)");
+    }
+    if (o.workspace) {
+        p->scratch = o.workspace;
+    } else {
+        e = hipMalloc(&p->scratch, pl.scratch_bytes);
+        if (e != hipSuccess) {
+            p->scratch = nullptr;
+            return hip_fail(e, "hipMalloc(plan scratch)");
+        }
+        p->own_scratch = true;
+    }
+    std::vector<unsigned char> host(pl.table_bytes);
+    fill_tables(pl, problems, host.data(), p->tables, static_cast<float *>(p->scratch));
+    e = hipMemcpy(p->tables, host.data(), pl.table_bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpy(plan tables)");
+    if (descs.size() > (size_t)kTopkInline) {
+        e = hipMalloc(reinterpret_cast<void **>(&p->topk_dev), descs.size() * sizeof(TopkDesc));
+        if (e != hipSuccess) {
+            p->topk_dev = nullptr;
+            return hip_fail(e, "hipMalloc(plan top-k)");
+        }
+        e = hipMemcpy(p->topk_dev, descs.data(), descs.size() * sizeof(TopkDesc), hipMemcpyHostToDevice);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipMemcpy(plan top-k)");
+    }
+    p->n_problems = n_problems;
+    p->d = d;
+    p->dtype = o.dtype;
+    p->kernel = pl.kernel;
+    p->rt = pl.rt;
+    p->n_items = (int)pl.items.size();
+    p->max_keys = pl.max_keys;
+    p->topk = std::move(descs);
+    AttnArgs &args = p->args;
+    args.probs = reinterpret_cast<const ProbDesc *>(p->tables + pl.off_probs);
+    args.items = reinterpret_cast<const ItemDesc *>(p->tables + pl.off_items);
+    args.H = H;
+    args.H_kv = H_kv;
+    args.G = H / H_kv;
+    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
+    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    *out = p.release();
+    return CRKV_OK;
+}
+
+int plan_launch(const crkv_plan *p, void *stream_ptr, void *const *timing_events)
+{
+    if (!p)
+        return fail(CRKV_E_INVAL, "plan must be non-null");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != p->device)
+        return fail(CRKV_E_INVAL, "plan was made on device %d, the current device is %d", p->device, dev);
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    if (timing_events && timing_events[0])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[0]), stream);
+    if (e == hipSuccess)
+        e = p->dtype != CRKV_BF16        ? launch_attn_f32(p->d, p->args, p->n_items, stream)
+            : p->kernel == kBf16Wave ? launch_attn_bf16_wave(p->d, p->rt, p->args, p->n_items, stream)
+                                     : launch_attn_bf16_pair(p->d, p->rt, p->args, p->n_items, stream);
+    if (e == hipSuccess && timing_events && timing_events[1])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[1]), stream);
+    if (e == hipSuccess)
+        e = launch_combine(p->args.probs, p->n_problems, p->max_keys, stream);
+    if (e == hipSuccess && !p->topk.empty()) {
+        if (p->topk.size() == 1)
+            e = launch_topk_one(p->topk[0], stream);
+        else if (p->topk.size() <= (size_t)kTopkInline)
+            e = launch_topk_inline(p->topk.data(), (int)p->topk.size(), stream);
+        else
+            e = launch_topk_batched(p->topk_dev, (int)p->topk.size(), stream);
+    }
+    return e == hipSuccess ? CRKV_OK : hip_fail(e, "plan launch");
+}
+
 // ------------------------------------------------------------ 8-bit segments
 size_t q8_bytes(int H_kv, int len, int d, int kind)
 {
@@ -1088,6 +1236,34 @@ int run_quantize(const crkv_q8_seg *segs, int n, int H_kv, int d, const crkv_opt
 }
 
 extern "C" {
+
+int crkv_plan_create(const crkv_problem *problems, int n_problems, int H, int H_kv, int d, const int32_t *k,
+                     int32_t *const *idx, const crkv_opts *opts, crkv_plan **plan)
+{
+    return plan_create(problems, n_problems, H, H_kv, d, k, idx, opts, plan);
+}
+
+int crkv_plan_launch(const crkv_plan *plan, void *stream, void *const *timing_events)
+{
+    return plan_launch(plan, stream, timing_events);
+}
+
+int crkv_plan_destroy(crkv_plan *plan)
+{
+    if (!plan)
+        return CRKV_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    const bool other = e == hipSuccess && dev != plan->device;
+    if (other)
+        e = hipSetDevice(plan->device);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();   // no launch of the plan may still read its memory
+    plan_free(plan);
+    if (other)
+        (void)hipSetDevice(dev);
+    return e == hipSuccess ? CRKV_OK : hip_fail(e, "plan destroy");
+}
 
 size_t crkv_q8_bytes(int H_kv, int len, int d, int kind) { return q8_bytes(H_kv, len, d, kind); }
 

@@ -29,8 +29,13 @@ document chunk of the 32 layers from positions 0 .. 2499 to their place in the
 concatenation (offsets 2500, 5000, 7500; the first chunk stays): one
 rotary re-positioning launch over all of them.
 
+With --config tiny or llama2_7b_layer (single small problems, bound by
+launch latency) the line also holds `graph`: the same step planned once
+(crkv_plan_create) and replayed from a captured graph.
+
 Prints one JSON line. The roofline object is for the attention kernel alone,
-timed with HIP events recorded on its stream around every launch.
+timed with HIP events recorded on its stream around every launch (mean, and
+the median / p10 / p90 over the timed steps).
 """
 from __future__ import annotations
 
@@ -54,6 +59,7 @@ SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
 METRIC_ROPE = "re-positioned key-layers/s (rotary shift of cached keys); % of HBM roofline"
 ROPE_CONFIGS = {"llama3_8b_rope_shift_32l": "llama3_8b_gqa_32l"}
 Q8_CONFIGS = {"llama3_8b_decode_q8_32l": "llama3_8b_decode_32l"}
+GRAPH_CONFIGS = ("tiny", "llama2_7b_layer")   # launch-bound: also timed as graph replays
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -519,12 +525,14 @@ def main():
     achieved_tf = flops / (k_ms * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     traffic = measured_traffic(args.config, "decode" if decode else "attn")
+    p10, p50, p90 = (float(x) for x in np.percentile(kern_ms, [10, 50, 90]))
     hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
            "kernel": plan["kernel"] if decode else "attn_%s_kernel" % plan["kernel"],
            "row_tiles": plan["row_tiles"],
            "workgroups": plan["workgroups"],
-           "kernel_ms": round(k_ms, 4), "alg_bytes_per_launch": nbytes}
+           "kernel_ms": round(k_ms, 4), "kernel_ms_p50": round(p50, 4), "kernel_ms_p10": round(p10, 4),
+           "kernel_ms_p90": round(p90, 4), "alg_bytes_per_launch": nbytes}
     mfma = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4),
             "alg_flops_per_launch": flops, "visible_pairs": npairs}
@@ -549,10 +557,40 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic", "config": cfg, "roofline": primary, "roofline_other": secondary,
            "kv_tokens_per_step": tokens}
+    if args.config in GRAPH_CONFIGS and not decode:
+        rec["graph"] = graph_replay(args, torch, crkv, wl, problems, ks, idx, tokens)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)
+
+
+def graph_replay(args, torch, crkv, wl, problems, ks, idx, tokens):
+    """The step (attention + impact combine + top-k) planned once and captured
+    into a graph; W replays untimed, then K timed between synchronisations."""
+    plan = crkv.Plan(problems, wl.H, wl.H_kv, wl.d, ks=ks, idxs=idx, mode=wl.mode)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.launch()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del g
+    plan.destroy()
+    return {"value": round(tokens / (wall / args.steps), 1), "unit": "KV tokens/s",
+            "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "how": "crkv_plan_create once; one captured crkv_plan_launch replayed per step"}
 
 
 if __name__ == "__main__":

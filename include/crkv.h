@@ -155,6 +155,31 @@ int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_
  * in double. Returns -1 if n_doc < 0 or r is not in [0, 1]. */
 int64_t crkv_budget(int64_t n_doc, double r);
 
+/*
+ * A batched attention call planned once, for launch-bound shapes and for
+ * capture into a hipGraph (the per-call path uploads its tables through a
+ * ring of reused buffers, which a replayed graph must not depend on).
+ * crkv_plan_create validates like crkv_attn_chunks_batched, builds the plan,
+ * allocates its device tables and impact partials (or uses opts->workspace,
+ * which must then outlive the plan) and copies the tables synchronously; the
+ * problems' device buffers (Q, segments, out, impact) are fixed into the
+ * plan. k (host, n_problems entries, 0 = no selection for that problem) and
+ * idx (host array of device int32 [k[i]] pointers) add the top-k of each
+ * problem's document impact, as crkv_topk_batched; pass k = NULL for none.
+ * crkv_plan_launch enqueues the attention kernel, the impact combine and the
+ * top-k on `stream` and nothing else (no allocation, copy or host wait), on
+ * the device the plan was made on (else CRKV_E_INVAL); timing_events (NULL
+ * or a hipEvent_t pair) bracket the attention kernel. Launches of one plan
+ * share its partials: concurrent launches of the same plan race.
+ * crkv_plan_destroy waits for the device, then frees the plan (NULL: no-op).
+ */
+typedef struct crkv_plan crkv_plan;
+
+int crkv_plan_create(const crkv_problem *problems, int n_problems, int H, int H_kv, int d, const int32_t *k,
+                     int32_t *const *idx, const crkv_opts *opts, crkv_plan **plan);
+int crkv_plan_launch(const crkv_plan *plan, void *stream, void *const *timing_events);
+int crkv_plan_destroy(crkv_plan *plan);
+
 /* Bytes of device scratch a crkv_attn_chunks_batched call with these
  * arguments needs when the caller passes opts->workspace (256-byte aligned
  * pointer). Returns 0 if the arguments are invalid. */

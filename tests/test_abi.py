@@ -284,3 +284,28 @@ def test_q8_dtype_is_decode_only(crkv_lib):
     with pytest.raises(crkv.CrkvError) as e:
         crkv.crkv_decode_chunks_batched([p], 8, 2, 128, dtype=5)
     assert e.value.status == -2
+
+
+def test_plan_create_rejects_invalid_arguments(crkv_lib):
+    """Validation comes before any allocation: these calls touch no device."""
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    o.dtype = crkv.CRKV_BF16
+    p = crkv._Problem(FAKE, [FAKE, FAKE], [FAKE, FAKE], [64, 16], 16, FAKE, FAKE)
+    arr = (crkv.crkv_problem * 1)(p.c)
+    h = ctypes.c_void_p()
+    L = crkv_lib
+    assert L.crkv_plan_create(arr, 1, 8, 2, 128, None, None, ctypes.byref(o), None) == -1       # no output
+    assert L.crkv_plan_create(arr, 1, 8, 3, 128, None, None, ctypes.byref(o), ctypes.byref(h)) == -1
+    assert L.crkv_plan_create(arr, 1, 8, 2, 96, None, None, ctypes.byref(o), ctypes.byref(h)) == -2
+    k = (ctypes.c_int32 * 1)(6)
+    assert L.crkv_plan_create(arr, 1, 8, 2, 128, k, None, ctypes.byref(o), ctypes.byref(h)) == -1  # k, no idx
+    idx = (ctypes.c_void_p * 1)(FAKE)
+    k[0] = 65                                                                                       # k > N_doc
+    assert L.crkv_plan_create(arr, 1, 8, 2, 128, k, idx, ctypes.byref(o), ctypes.byref(h)) == -1
+    o.dtype = crkv.CRKV_KV_Q8
+    k[0] = 6
+    assert L.crkv_plan_create(arr, 1, 8, 2, 128, k, idx, ctypes.byref(o), ctypes.byref(h)) == -1
+    assert h.value is None
+    assert L.crkv_plan_launch(None, None, None) == -1
+    assert L.crkv_plan_destroy(None) == 0
