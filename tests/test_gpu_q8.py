@@ -195,3 +195,46 @@ def test_q8_error_against_the_bf16_cache():
     rel = float((np.abs(got - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
     say("  8-bit cache vs bf16 cache: row-relative max error %.3g" % rel)
     assert rel < 0.05
+
+
+def test_q8_decode_loop_over_a_growing_segment():
+    """The documented decode loop: each step appends the new token's K/V to
+    the last segment, quantises that segment again (its K channel scales
+    cover the tokens present) and decodes over the 8-bit cache; every step
+    against the oracle over the same dequantised cache."""
+    wl = workloads.custom(470, [300, 128], 1, 8, 2, 128, dtype="bf16", gen_len=20, k_outliers=4)
+    full = wl.problems[0]
+    H_kv, d = wl.H_kv, wl.d
+    doc_lens = full.lens[:-1]
+    from gpu_util import t_dev
+    dev_K = [t_dev(k, "bf16") for k in full.K]
+    dev_V = [t_dev(v, "bf16") for v in full.V]
+    docs_q = []
+    segs = []
+    for c, n in enumerate(doc_lens):
+        bk = torch.empty(crkv.crkv_q8_bytes(H_kv, n, d, crkv.CRKV_Q8_K), dtype=torch.uint8, device=DEV)
+        bv = torch.empty(crkv.crkv_q8_bytes(H_kv, n, d, crkv.CRKV_Q8_V), dtype=torch.uint8, device=DEV)
+        segs += [(dev_K[c], bk, n, crkv.CRKV_Q8_K), (dev_V[c], bv, n, crkv.CRKV_Q8_V)]
+        docs_q.append((bk, bv))
+    crkv.crkv_quantize_q8(segs, H_kv, d)
+    total = full.lens[-1]
+    for step, n in enumerate(range(total - 3, total + 1)):   # the last segment grows by one token a step
+        kl = np.ascontiguousarray(full.K[-1][:, :n])
+        vl = np.ascontiguousarray(full.V[-1][:, :n])
+        kdev, vdev = t_dev(kl, "bf16"), t_dev(vl, "bf16")
+        bk = torch.empty(crkv.crkv_q8_bytes(H_kv, n, d, crkv.CRKV_Q8_K), dtype=torch.uint8, device=DEV)
+        bv = torch.empty(crkv.crkv_q8_bytes(H_kv, n, d, crkv.CRKV_Q8_V), dtype=torch.uint8, device=DEV)
+        crkv.crkv_quantize_q8([(kdev, bk, n, crkv.CRKV_Q8_K), (vdev, bv, n, crkv.CRKV_Q8_V)], H_kv, d)
+        prob = workloads.Problem(K=list(full.K[:-1]) + [kl], V=list(full.V[:-1]) + [vl],
+                                 lens=list(doc_lens) + [n], q_len=1,
+                                 Q=workloads.round_bf16(np.random.default_rng(480 + step).standard_normal(
+                                     (wl.H, 1, d)).astype(np.float32)))
+        Q = t_dev(prob.Q, "bf16")
+        out = torch.empty_like(Q)
+        pd = dict(Q=Q, chunk_K=[b for b, _ in docs_q] + [bk], chunk_V=[b for _, b in docs_q] + [bv],
+                  chunk_len=prob.lens, q_len=1, out=out, impact=None)
+        crkv.crkv_decode_chunks_batched([pd], wl.H, H_kv, d, dtype=crkv.CRKV_KV_Q8)
+        torch.cuda.synchronize()
+        ref = q8.decode(prob, wl.H, H_kv, d)
+        err = check_out(to_host(out), ref, "bf16", "q8-loop step %d" % step)
+        say("  step %d (%d own keys): out err %.3g" % (step, n, err))
