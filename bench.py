@@ -123,6 +123,20 @@ def measured_traffic(config, kind="attn"):
     return t.get("bytes_per_launch")
 
 
+def measured_mfma(config):
+    """Executed bf16 MFMA FLOPs, matrix-core busy share and clock of the timed
+    attention kernel from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_%s_mfma.json" % config)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_source_sha("attn"):
+        return None
+    return {k: t[k] for k in ("executed_flops_per_launch", "mfma_busy_pct", "clock_ghz")}
+
+
 class HipEvents:
     """hipEvent_t pairs from the HIP runtime torch has loaded."""
 
@@ -239,7 +253,7 @@ def bench_q8_decode(args, torch, crkv, workloads):
     rec = {"metric": METRIC_DECODE, "value": round(tokens / (wall / args.steps), 1), "unit": "KV tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "int8 (K/V), bf16 (Q, out), f32 accumulate", "data": "synthetic",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": cfg,
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config, "q8"),
@@ -535,7 +549,8 @@ def main():
            "kernel_ms_p90": round(p90, 4), "alg_bytes_per_launch": nbytes}
     mfma = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4),
-            "alg_flops_per_launch": flops, "visible_pairs": npairs}
+            "alg_flops_per_launch": flops, "visible_pairs": npairs,
+            "counters": None if decode else measured_mfma(args.config)}
     # the benchmark spec states the short-query (10k-document) target against HBM
     # and the large-batch one against MFMA
     primary, secondary = (mfma, hbm) if args.config in ("ragged_70b", "cross_doc") else (hbm, mfma)
