@@ -31,9 +31,10 @@ document chunk of the 32 layers from positions 0 .. 2499 to their place in the
 concatenation (offsets 2500, 5000, 7500; the first chunk stays): one
 rotary re-positioning launch over all of them.
 
-With --config tiny or llama2_7b_layer (single small problems, bound by
-launch latency) the line also holds `graph`: the same step planned once
-(crkv_plan_create) and replayed from a captured graph.
+For the attention workloads the line also holds `graph`: the same step
+planned once (crkv_plan_create) and replayed from a captured graph, which
+removes the per-call host planning and launch gaps (most visible on the
+launch-bound tiny and llama2_7b_layer shapes).
 
 Prints one JSON line. The roofline object is for the attention kernel alone,
 timed with HIP events recorded on its stream around every launch (mean, and
@@ -61,7 +62,7 @@ SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
 METRIC_ROPE = "re-positioned key-layers/s (rotary shift of cached keys); % of HBM roofline"
 ROPE_CONFIGS = {"llama3_8b_rope_shift_32l": "llama3_8b_gqa_32l"}
 Q8_CONFIGS = {"llama3_8b_decode_q8_32l": "llama3_8b_decode_32l"}
-GRAPH_CONFIGS = ("tiny", "llama2_7b_layer")   # launch-bound: also timed as graph replays
+SMALL_CONFIGS = ("tiny", "llama2_7b_layer")   # single small problems: the oracle is also timed on one core
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -185,7 +186,7 @@ def cpu_baseline(wl, budget_s=15.0):
     rec = {"value": tokens / elapsed, "unit": "KV tokens/s", "cores": oracle.max_threads(),
            "kind": "oracle", "sample": "problems 0..%d of %d (%s), %.1f s of CPU time"
            % (n - 1, len(wl.problems), wl.spec.name if wl.spec else "custom", elapsed)}
-    if wl.spec and wl.spec.name in GRAPH_CONFIGS:   # the small single-problem shapes: one core too
+    if wl.spec and wl.spec.name in SMALL_CONFIGS:
         t0 = time.perf_counter()
         oracle.run_workload(wl, problems=[0], n_threads=1)
         rec["single_thread_value"] = wl.problems[0].n_keys / (time.perf_counter() - t0)
@@ -579,7 +580,7 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic", "config": cfg, "roofline": primary, "roofline_other": secondary,
            "kv_tokens_per_step": tokens}
-    if args.config in GRAPH_CONFIGS and not decode:
+    if not decode:
         rec["graph"] = graph_replay(args, torch, crkv, wl, problems, ks, idx, tokens)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
