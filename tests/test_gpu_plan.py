@@ -146,3 +146,23 @@ def test_plan_with_workspace_and_destroy_twice():
         plan.launch()
     with pytest.raises(crkv.CrkvError):
         crkv.Plan(dw.problems, wl.H, wl.H_kv, wl.d, workspace=ws, workspace_bytes=nbytes - 256)
+
+
+def test_plan_with_more_problems_than_inline_topk():
+    """70 problems: the plan keeps the top-k descriptors in device memory
+    (more than fit in kernel arguments); equal to the per-call path."""
+    wl = workloads.custom(703, [40, 25], 8, 4, 2, 64, dtype="bf16", n_problems=70, r=0.2)
+    dw = DeviceWorkload(wl)
+    ks, idx = selections(dw)
+    dw.attn()
+    crkv.crkv_topk_batched([p["impact"] for p in dw.problems], [p.n_doc for p in wl.problems], ks, idx)
+    torch.cuda.synchronize()
+    ref = outputs(dw, idx)
+    clear(dw, idx)
+    plan = crkv.Plan(dw.problems, wl.H, wl.H_kv, wl.d, ks=ks, idxs=idx)
+    plan.launch()
+    torch.cuda.synchronize()
+    same(outputs(dw, idx), ref)
+    ro, ri, _ = oracle.attn(wl.problems[69], wl.H, wl.H_kv, wl.d, "bf16", "query")
+    check_out(to_host(dw.problems[69]["out"]), ro, "bf16", "many[69]")
+    plan.destroy()
