@@ -85,7 +85,8 @@ def check_impact(imp, ref, label=""):
         i = int(np.argmax(np.abs(imp - ref) / np.maximum(np.abs(ref), 1e-300)))
         raise AssertionError("%s impact: %d elements off; worst at %d: %r vs %r"
                              % (label, int(bad.sum()), i, imp[i], ref[i]))
-    return float((np.abs(imp - ref) / np.abs(ref)).max())
+    nz = ref != 0   # keys no counted row attends to have impact 0 on both sides (checked above)
+    return float((np.abs(imp - ref)[nz] / np.abs(ref[nz])).max()) if nz.any() else 0.0
 
 
 def check_selection(gpu_idx, ref_idx, ref_imp_doc, label=""):
