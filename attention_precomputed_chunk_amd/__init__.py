@@ -23,8 +23,7 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# CRKV_LIB_PATH selects another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("CRKV_LIB_PATH") or os.path.join(HERE, "libcrkv.so")
+LIB_PATH = os.path.join(HERE, "libcrkv.so")
 
 CRKV_OK = 0
 CRKV_E_INVAL = -1

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -59,12 +60,13 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        flags = HIPCC_FLAGS + (KERNEL_FLAGS if src in KERNEL_SOURCES else [])
-        _run([hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(objdir, src.replace(".hip", ".o")) for src in SOURCES]
+    cmds = [[hipcc()] + HIPCC_FLAGS + (KERNEL_FLAGS if src in KERNEL_SOURCES else []) +
+            ["-c", os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0")) or (os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -62,7 +62,10 @@ SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
 METRIC_ROPE = "re-positioned key-layers/s (rotary shift of cached keys); % of HBM roofline"
 ROPE_CONFIGS = {"llama3_8b_rope_shift_32l": "llama3_8b_gqa_32l"}
 Q8_CONFIGS = {"llama3_8b_decode_q8_32l": "llama3_8b_decode_32l"}
-SMALL_CONFIGS = ("tiny", "llama2_7b_layer")   # single small problems: the oracle is also timed on one core
+SMALL_CONFIGS = ("tiny", "llama2_7b_layer")
+DEFAULT_CONFIG = "llama3_8b_gqa_32l"
+# timed after the headline in the default run and reported under "configs"
+OTHER_ATTN_CONFIGS = ("ragged_70b", "cross_doc", "llama2_7b_layer", "tiny")   # single small problems: the oracle is also timed on one core
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
@@ -443,8 +446,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama3_8b_gqa_32l")
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="with the default workload, skip timing the other attention workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -483,8 +488,26 @@ def main():
         bench_q8_decode(args, torch, crkv, workloads)
         return
 
-    log("generating %s" % args.config)
-    wl = workloads.generate(args.config)
+    rec = bench_attention(args, torch, crkv, workloads, args.config, args.steps, args.warmup,
+                          with_cpu=not args.no_cpu_baseline)
+    if args.config == DEFAULT_CONFIG and not args.no_other_configs:
+        # the other attention workloads of the contract, timed in the same
+        # process after the headline (their own lines of the record)
+        rec["configs"] = {}
+        for name in OTHER_ATTN_CONFIGS:
+            sub = bench_attention(args, torch, crkv, workloads, name, args.steps, args.warmup, with_cpu=False)
+            rec["configs"][name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                                        "roofline", "roofline_other", "graph",
+                                                        "kv_tokens_per_step")}
+    print(json.dumps(rec), flush=True)
+
+
+def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu):
+    """Attention + impact combine + top-k of one workload: `steps` timed
+    steps after `warmup`, the attention kernel bracketed by HIP events on the
+    library's launch stream; returns the record (not printed)."""
+    log("generating %s" % name)
+    wl = workloads.generate(name)
     dev = "cuda:0"
 
     def up(a):
@@ -510,7 +533,7 @@ def main():
         plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
     log("plan: %s" % plan)
     ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
 
     decode = bool(wl.spec.decode)
     batch = crkv.Batch(problems)   # marshalled once: the same tensors every step
@@ -523,13 +546,13 @@ def main():
                                       timing_events=events)
         crkv.crkv_topk_batched(imps, ns, ks, idx)
 
-    log("warmup %d" % args.warmup)
-    for _ in range(args.warmup):
+    log("warmup %d" % warmup)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log("timing %d steps" % args.steps)
+    log("timing %d steps" % steps)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(pairs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -538,15 +561,15 @@ def main():
         ev.destroy(a)
         ev.destroy(b)
 
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     tokens = workloads.kv_tokens(wl)
-    value = tokens / (wall / args.steps)
+    value = tokens / (wall / steps)
     nbytes, flops, npairs = algorithmic_work(wl)
     k_ms = float(np.mean(kern_ms))
     achieved_gbs = nbytes / (k_ms * 1e-3) / 1e9
     achieved_tf = flops / (k_ms * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    traffic = measured_traffic(args.config, "decode" if decode else "attn")
+    traffic = measured_traffic(name, "decode" if decode else "attn")
     p10, p50, p90 = (float(x) for x in np.percentile(kern_ms, [10, 50, 90]))
     hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -558,12 +581,12 @@ def main():
     mfma = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4),
             "alg_flops_per_launch": flops, "visible_pairs": npairs,
-            "counters": None if decode else measured_mfma(args.config)}
+            "counters": None if decode else measured_mfma(name)}
     # the short-query workloads are reported against HBM first, the large
     # row-count ones (ragged batch, cross-document) against the matrix cores
-    primary, secondary = (mfma, hbm) if args.config in ("ragged_70b", "cross_doc") else (hbm, mfma)
+    primary, secondary = (mfma, hbm) if name in ("ragged_70b", "cross_doc") else (hbm, mfma)
     spec = wl.spec
-    cfg = {"workload": args.config, "problems": len(wl.problems), "H": wl.H, "H_kv": wl.H_kv,
+    cfg = {"workload": name, "problems": len(wl.problems), "H": wl.H, "H_kv": wl.H_kv,
            "d": wl.d, "mode": wl.mode, "r": wl.r}
     if spec.chunk_lens:
         cfg.update({"chunks": len(spec.chunk_lens), "chunk_len": spec.chunk_lens[0],
@@ -576,19 +599,22 @@ def main():
     if decode:
         cfg["step"] = "decode"
     rec = {"metric": METRIC_DECODE if decode else METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic", "config": cfg, "roofline": primary, "roofline_other": secondary,
            "kv_tokens_per_step": tokens}
     if not decode:
-        rec["graph"] = graph_replay(args, torch, crkv, wl, problems, ks, idx, tokens)
-    if not args.no_cpu_baseline:
+        rec["graph"] = graph_replay(steps, warmup, torch, crkv, wl, problems, ks, idx, tokens)
+    if with_cpu:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(wl)
-    print(json.dumps(rec), flush=True)
+    del problems, batch, imps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
-def graph_replay(args, torch, crkv, wl, problems, ks, idx, tokens):
+def graph_replay(steps, warmup, torch, crkv, wl, problems, ks, idx, tokens):
     """The step (attention + impact combine + top-k) planned once and captured
     into a graph; W replays untimed, then K timed between synchronisations."""
     plan = crkv.Plan(problems, wl.H, wl.H_kv, wl.d, ks=ks, idxs=idx, mode=wl.mode)
@@ -601,18 +627,18 @@ def graph_replay(args, torch, crkv, wl, problems, ks, idx, tokens):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         plan.launch()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         g.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     del g
     plan.destroy()
-    return {"value": round(tokens / (wall / args.steps), 1), "unit": "KV tokens/s",
-            "ms_per_step": round(wall * 1e3 / args.steps, 4),
+    return {"value": round(tokens / (wall / steps), 1), "unit": "KV tokens/s",
+            "ms_per_step": round(wall * 1e3 / steps, 4),
             "how": "crkv_plan_create once; one captured crkv_plan_launch replayed per step"}
 
 

@@ -10,6 +10,9 @@ Tolerances (float results):
     whose oracle impact is within 1e-5 (relative) of the oracle's k-th value;
     fed the same fp32 impact, the GPU selection must equal the oracle's exactly.
 """
+import os
+import sys
+
 import numpy as np
 import torch
 
@@ -66,6 +69,7 @@ class DeviceWorkload:
 
 def check_out(out, ref, dtype, label=""):
     out = np.asarray(out, dtype=np.float64)
+    assert np.isfinite(out).all(), "%s out has %d non-finite elements" % (label, int((~np.isfinite(out)).sum()))
     if dtype == "f32":
         err = np.abs(out - ref).max()
         assert err <= 1e-5, "%s out max-abs error %.3g > 1e-5" % (label, err)
@@ -80,7 +84,9 @@ def check_out(out, ref, dtype, label=""):
 
 def check_impact(imp, ref, label=""):
     imp = np.asarray(imp, dtype=np.float64)
-    bad = np.abs(imp - ref) > 1e-4 * np.abs(ref)
+    # written as "not within" so that a NaN (an unwritten element: the tests
+    # pre-fill impact with NaN) counts as off
+    bad = ~(np.abs(imp - ref) <= 1e-4 * np.abs(ref))
     if bad.any():
         i = int(np.argmax(np.abs(imp - ref) / np.maximum(np.abs(ref), 1e-300)))
         raise AssertionError("%s impact: %d elements off; worst at %d: %r vs %r"
@@ -97,3 +103,59 @@ def check_selection(gpu_idx, ref_idx, ref_imp_doc, label=""):
     for i in g ^ r:
         assert abs(ref_imp_doc[i] - t) <= 1e-5 * abs(t), \
             "%s index %d selected differently and is not a boundary tie" % (label, i)
+
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name, wl):
+    """The oracle's impact (float64) and top-k of every problem of workload
+    `name`, stored by tests/golden/make_full_golden.py (which calls only the
+    oracle and the input generator), after checking that the stored input
+    fingerprints match the workload generated here."""
+    sys.path.insert(0, GOLDEN_DIR)
+    from make_full_golden import fingerprint
+    g = np.load(os.path.join(GOLDEN_DIR, "full_%s.npz" % name), allow_pickle=False)
+    assert str(g["workload"]) == name
+    n = int(g["n_problems"])
+    assert n == len(wl.problems), "golden has %d problems, workload %d" % (n, len(wl.problems))
+    res = []
+    for pi, prob in enumerate(wl.problems):
+        assert str(g["fp_%d" % pi]) == fingerprint(prob), \
+            "%s problem %d: inputs differ from those the golden file was written for" % (name, pi)
+        res.append((g["impact_%d" % pi], g["idx_%d" % pi], int(g["k_%d" % pi])))
+    return res
+
+
+def check_sorted_selection(idx, imp_doc, label=""):
+    """The GPU output order is (value desc, index asc) on its own impact."""
+    v = imp_doc[idx]
+    assert np.all(v[:-1] >= v[1:]), "%s not sorted by value" % label
+    ties = v[:-1] == v[1:]
+    assert np.all(idx[:-1][ties] < idx[1:][ties]), "%s ties not in index order" % label
+
+
+def compare_golden(dw, gidx, golden, label=""):
+    """Every problem's impact (all N keys) and selection against the stored
+    oracle results; then the GPU top-k fed the oracle's own float32 impact of
+    every problem must reproduce the oracle's indices exactly. Returns the
+    worst impact relative error."""
+    wl = dw.wl
+    worst = 0.0
+    for pi, (prob, (imp_ref, idx_ref, k)) in enumerate(zip(wl.problems, golden)):
+        lab = "%s[problem %d]" % (label, pi)
+        imp = dw.problems[pi]["impact"].cpu().numpy()
+        worst = max(worst, check_impact(imp, imp_ref, lab))
+        n_doc = prob.n_doc
+        g = gidx[pi].cpu().numpy()
+        assert len(g) == k
+        check_selection(g, idx_ref, imp_ref[:n_doc], lab)
+        check_sorted_selection(g, imp[:n_doc], lab)
+    exact = [torch.from_numpy(imp_ref[:p.n_doc].astype(np.float32)).to(DEV)
+             for p, (imp_ref, _, _) in zip(wl.problems, golden)]
+    out_idx = [torch.full((k,), -1, dtype=torch.int32, device=DEV) for (_, _, k) in golden]
+    crkv.crkv_topk_batched(exact, [p.n_doc for p in wl.problems], [k for (_, _, k) in golden], out_idx)
+    torch.cuda.synchronize()
+    for pi, (oi, (_, idx_ref, _)) in enumerate(zip(out_idx, golden)):
+        np.testing.assert_array_equal(oi.cpu().numpy(), idx_ref, err_msg="%s[problem %d] top-k" % (label, pi))
+    return worst
