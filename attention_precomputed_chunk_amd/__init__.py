@@ -77,6 +77,7 @@ class crkv_q8_seg(ctypes.Structure):
 _lib = None
 
 DECLARED = ["crkv_plan_create", "crkv_plan_launch", "crkv_plan_destroy", "crkv_q8_bytes", "crkv_quantize_q8", "crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
+            "crkv_attn_chunks_batched_static", "crkv_static_scratch_bytes",
             "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
             "crkv_decode_chunks_batched", "crkv_decode_workspace_size", "crkv_gather_kv",
             "crkv_scatter_kv", "crkv_rope_shift",
@@ -105,6 +106,11 @@ def lib():
         L.crkv_attn_chunks_batched.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
                                                ctypes.POINTER(crkv_opts)]
         L.crkv_attn_chunks_batched.restype = c_int
+        L.crkv_attn_chunks_batched_static.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                                      ctypes.POINTER(crkv_opts)]
+        L.crkv_attn_chunks_batched_static.restype = c_int
+        L.crkv_static_scratch_bytes.argtypes = []
+        L.crkv_static_scratch_bytes.restype = ctypes.c_size_t
         L.crkv_topk.argtypes = [vp, c_int, c_int, vp, ctypes.POINTER(crkv_opts)]
         L.crkv_topk.restype = c_int
         L.crkv_topk_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -258,6 +264,20 @@ def crkv_attn_chunks_batched(problems: Sequence[dict], H: int, H_kv: int, d: int
     o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream,
                   workspace, workspace_bytes, timing_events)
     _check(lib().crkv_attn_chunks_batched(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+def crkv_attn_chunks_batched_static(problems: Sequence[dict], H: int, H_kv: int, d: int,
+                                    mode: str = "query", stream=None, timing_events=None,
+                                    dtype: Optional[int] = None):
+    """crkv_attn_chunks_batched with the library's static device scratch (no
+    device allocation; for callers that cannot allocate)."""
+    keep, arr = _problems(problems)
+    o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream, None, 0, timing_events)
+    _check(lib().crkv_attn_chunks_batched_static(arr, len(keep), H, H_kv, d, ctypes.byref(o)))
+
+
+def crkv_static_scratch_bytes() -> int:
+    return int(lib().crkv_static_scratch_bytes())
 
 
 class Plan:

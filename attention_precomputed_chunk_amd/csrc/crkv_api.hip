@@ -659,6 +659,68 @@ int check_topk_args(const float *impact, int n, int k, const int32_t *idx, int w
     return CRKV_OK;
 }
 
+// Enqueues the attention kernel the plan chose and the impact combine, with
+// the plan's tables at `dev` (device copy already enqueued on `stream`).
+hipError_t launch_planned(const Plan &pl, int n_problems, int H, int H_kv, int d, const crkv_opts &o,
+                          const unsigned char *dev, hipStream_t stream)
+{
+    AttnArgs args{};
+    args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
+    args.items = reinterpret_cast<const ItemDesc *>(dev + pl.off_items);
+    args.H = H;
+    args.H_kv = H_kv;
+    args.G = H / H_kv;
+    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
+    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+
+    hipError_t e = hipSuccess;
+    if (o.timing_events[0])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
+    if (e == hipSuccess)
+        e = o.dtype != CRKV_BF16      ? launch_attn_f32(d, args, (int)pl.items.size(), stream)
+            : pl.kernel == kBf16Wave ? launch_attn_bf16_wave(d, pl.rt, args, (int)pl.items.size(), stream)
+                                     : launch_attn_bf16_pair(d, pl.rt, args, (int)pl.items.size(), stream);
+    if (e == hipSuccess && o.timing_events[1])
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
+    if (e == hipSuccess)
+        e = launch_combine(args.probs, n_problems, pl.max_keys, stream);
+    return e;
+}
+
+// ------------------------------------------------------------ static scratch
+// Device memory for crkv_attn_chunks_batched_static, the entry point for
+// callers that cannot allocate: a file-scope array each device holds once the
+// library's code is loaded on it, until the process ends. In host code the
+// array's name is only a stand-in, so its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and kept; host
+// code passes that address, never the name, to kernels and copies. Every call
+// on a device shares the one array and leaves its contents behind; calls that
+// overlap on one device (different streams, or threads) race.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;
+std::map<int, unsigned char *> g_static_ptr;
+
+int static_scratch(unsigned char **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    auto it = g_static_ptr.find(dev);
+    if (it == g_static_ptr.end()) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        it = g_static_ptr.emplace(dev, static_cast<unsigned char *>(ptr)).first;
+    }
+    *out = it->second;
+    return CRKV_OK;
+}
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -1437,32 +1499,52 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
         scratch_release(sc, stream);
         return rc;
     }
-    AttnArgs args{};
-    args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
-    args.items = reinterpret_cast<const ItemDesc *>(dev + pl.off_items);
-    args.H = H;
-    args.H_kv = H_kv;
-    args.G = H / H_kv;
-    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
-    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-
-    hipError_t e = hipSuccess;
-    if (o.timing_events[0])
-        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
-    if (e == hipSuccess)
-        e = o.dtype != CRKV_BF16      ? launch_attn_f32(d, args, (int)pl.items.size(), stream)
-            : pl.kernel == kBf16Wave ? launch_attn_bf16_wave(d, pl.rt, args, (int)pl.items.size(), stream)
-                                     : launch_attn_bf16_pair(d, pl.rt, args, (int)pl.items.size(), stream);
-    if (e == hipSuccess && o.timing_events[1])
-        e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
-    if (e == hipSuccess)
-        e = launch_combine(args.probs, n_problems, pl.max_keys, stream);
+    const hipError_t e = launch_planned(pl, n_problems, H, H_kv, d, o, dev, stream);
     plan_release(lease, stream);
     scratch_release(sc, stream);
     if (e != hipSuccess)
         return hip_fail(e, "attention launch");
     return CRKV_OK;
 }
+
+int crkv_attn_chunks_batched_static(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                                    const crkv_opts *opts)
+{
+    const crkv_opts o = resolve(opts);
+    int rc = validate_batch(problems, n_problems, H, H_kv, d, o);
+    if (rc)
+        return rc;
+    if (o.workspace)
+        return fail(CRKV_E_INVAL, "crkv_attn_chunks_batched_static uses the library's static scratch: "
+                                  "opts.workspace must be NULL (pass a workspace to crkv_attn_chunks_batched)");
+    Plan pl;
+    build_plan(pl, problems, n_problems, H, H_kv, d, o);
+    // tables first, then the impact partials, each 256-byte aligned
+    const size_t partial_off = align_up(pl.table_bytes, 256);
+    const size_t need = partial_off + pl.scratch_bytes;
+    if (need > kStaticScratchBytes)
+        return fail(CRKV_E_UNSUPPORTED,
+                    "crkv_attn_chunks_batched_static: the call needs %zu bytes of scratch (tables %zu, impact "
+                    "partials %zu), above the static scratch of %zu bytes",
+                    need, pl.table_bytes, pl.scratch_bytes, kStaticScratchBytes);
+    unsigned char *base = nullptr;
+    rc = static_scratch(&base);
+    if (rc)
+        return rc;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(o.stream);
+    std::vector<unsigned char> host(pl.table_bytes);
+    fill_tables(pl, problems, host.data(), base, reinterpret_cast<float *>(base + partial_off));
+    // from pageable memory: the call returns once `host` has been read
+    hipError_t e = hipMemcpyAsync(base, host.data(), pl.table_bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync(static tables)");
+    e = launch_planned(pl, n_problems, H, H_kv, d, o, base, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "attention launch");
+    return CRKV_OK;
+}
+
+size_t crkv_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 int crkv_attn_chunks(const void *Q, const void *const *chunk_K, const void *const *chunk_V,
                      const int32_t *chunk_len, int m, int q_len, int H, int H_kv, int d, void *out,

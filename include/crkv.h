@@ -145,6 +145,31 @@ typedef struct crkv_problem {
 int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv,
                              int d, const crkv_opts *opts);
 
+/*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same batched
+ * attention as crkv_attn_chunks_batched (same kernels, same results bit for
+ * bit), with its plan tables and impact partials in a static device array
+ * the library holds on each device it runs on (crkv_static_scratch_bytes()
+ * bytes, 64 MiB, held until the process ends) instead of a workspace or a
+ * library-grown buffer. The call allocates no device or pinned host memory;
+ * it copies the plan tables from pageable host memory into the array with
+ * hipMemcpyAsync on opts->stream (the call returns once the host copy has
+ * been read). The first call on a device looks up the array's device
+ * address. opts->workspace must be NULL (else CRKV_E_INVAL). A call whose
+ * tables plus partials exceed the array returns CRKV_E_UNSUPPORTED before
+ * enqueuing anything (the 32-layer Llama-3-8B-shaped batch needs about
+ * 11 MB). Every call on a device shares the one array and leaves its
+ * contents behind (nothing in it has to start at zero): calls that overlap
+ * on one device, from different streams or threads, race; calls on one
+ * stream are ordered.
+ */
+int crkv_attn_chunks_batched_static(const crkv_problem *problems, int n_problems, int H, int H_kv,
+                                    int d, const crkv_opts *opts);
+
+/* Size in bytes of the static device array crkv_attn_chunks_batched_static uses. */
+size_t crkv_static_scratch_bytes(void);
+
 /* Top-k for n_problems vectors in one launch. impact and idx are host arrays
  * of device pointers; n and k are host arrays. Same contract as crkv_topk. */
 int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_t *k,

@@ -309,3 +309,39 @@ def test_plan_create_rejects_invalid_arguments(crkv_lib):
     assert h.value is None
     assert L.crkv_plan_launch(None, None, None) == -1
     assert L.crkv_plan_destroy(None) == 0
+
+
+def _static_call(crkv_lib, probs, H, H_kv, d, mode, workspace=None):
+    arr = (crkv.crkv_problem * len(probs))()
+    keep = []
+    for i, p in enumerate(probs):
+        m = len(p["chunk_len"]) - 1
+        k = (ctypes.c_void_p * (m + 1))(*p["chunk_K"])
+        v = (ctypes.c_void_p * (m + 1))(*p["chunk_V"])
+        ln = (ctypes.c_int32 * (m + 1))(*p["chunk_len"])
+        keep += [k, v, ln]
+        arr[i] = crkv.crkv_problem(p["Q"], k, v, ln, m, p["q_len"], p["out"], p["impact"])
+    o = crkv.crkv_opts()
+    crkv_lib.crkv_opts_init(ctypes.byref(o))
+    o.dtype = crkv.CRKV_BF16
+    o.mode = mode
+    o.workspace = workspace
+    rc = crkv_lib.crkv_attn_chunks_batched_static(arr, len(probs), H, H_kv, d, ctypes.byref(o))
+    return rc, crkv_lib.crkv_last_error().decode()
+
+
+def test_static_scratch_refusals(crkv_lib):
+    """crkv_attn_chunks_batched_static refuses, before touching any device, a
+    call whose tables and impact partials exceed its static scratch, and a
+    caller workspace; its invalid arguments fail like the per-call entry
+    point's."""
+    assert crkv.crkv_static_scratch_bytes() == 64 << 20
+    big = [_fake_problem([8192] * 8, 128, 32, 128) for _ in range(4)]
+    rc, msg = _static_call(crkv_lib, big, 32, 32, 128, 1)
+    assert rc == crkv.CRKV_E_UNSUPPORTED and "static scratch" in msg, msg
+    one = [_fake_problem([512] * 4, 64, 32, 128)]
+    rc, msg = _static_call(crkv_lib, one, 32, 32, 128, 0, workspace=0x100000)
+    assert rc == crkv.CRKV_E_INVAL and "workspace must be NULL" in msg, msg
+    bad = [dict(one[0], q_len=0)]
+    rc, msg = _static_call(crkv_lib, bad, 32, 32, 128, 0)
+    assert rc == crkv.CRKV_E_INVAL and "q_len" in msg, msg
