@@ -45,7 +45,7 @@ class CrkvError(RuntimeError):
 class crkv_opts(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("mode", ctypes.c_int), ("stream", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("timing_events", ctypes.c_void_p * 2)]
+                ("timing_events", ctypes.c_void_p * 2), ("deterministic", ctypes.c_int)]
 
 
 class crkv_problem(ctypes.Structure):

@@ -336,6 +336,8 @@ int check_opts(const crkv_opts &o)
         return fail(CRKV_E_INVAL, "opts.dtype %d is not CRKV_F32 or CRKV_BF16", o.dtype);
     if (o.mode < CRKV_IMPACT_QUERY_ROWS || o.mode > CRKV_IMPACT_ALL_ROWS)
         return fail(CRKV_E_INVAL, "opts.mode %d is not a crkv_mode", o.mode);
+    if (o.deterministic != 0 && o.deterministic != 1)
+        return fail(CRKV_E_INVAL, "opts.deterministic %d is not 0 or 1", o.deterministic);
     if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u))
         return fail(CRKV_E_INVAL, "workspace must be 256-byte aligned");
     return CRKV_OK;
@@ -1341,6 +1343,7 @@ void crkv_opts_init(crkv_opts *opts)
     memset(opts, 0, sizeof *opts);
     opts->dtype = CRKV_F32;
     opts->mode = CRKV_IMPACT_QUERY_ROWS;
+    opts->deterministic = 1;
 }
 
 int crkv_version(void) { return CRKV_VERSION; }
@@ -1565,6 +1568,8 @@ int crkv_attn_chunks(const void *Q, const void *const *chunk_K, const void *cons
 int crkv_topk(const float *impact, int n, int k, int32_t *idx, const crkv_opts *opts)
 {
     const crkv_opts o = resolve(opts);
+    if (o.deterministic != 0 && o.deterministic != 1)
+        return fail(CRKV_E_INVAL, "opts.deterministic %d is not 0 or 1", o.deterministic);
     int rc = check_topk_args(impact, n, k, idx, 0);
     if (rc)
         return rc;
@@ -1579,6 +1584,8 @@ int crkv_topk_batched(const float *const *impact, const int32_t *n, const int32_
                       int32_t *const *idx, int n_problems, const crkv_opts *opts)
 {
     const crkv_opts o = resolve(opts);
+    if (o.deterministic != 0 && o.deterministic != 1)
+        return fail(CRKV_E_INVAL, "opts.deterministic %d is not 0 or 1", o.deterministic);
     if (n_problems < 1)
         return fail(CRKV_E_INVAL, "n_problems = %d < 1", n_problems);
     if (!impact || !n || !k || !idx)

@@ -99,9 +99,16 @@ typedef struct crkv_opts {
     void *timing_events[2]; /* optional hipEvent_t pair recorded on `stream`
                                immediately before and after the attention
                                kernel (for measuring that kernel alone)         */
+    int deterministic;      /* 1 (the default) or 0; results are bit-identical
+                               from call to call either way: every reduction
+                               (impact partials, split ranges, top-k) runs in
+                               a fixed order without atomics, so there is no
+                               faster nondeterministic mode to select. Other
+                               values are CRKV_E_INVAL                          */
 } crkv_opts;
 
-/* Defaults: fp32, query-row mode, null stream, library-managed scratch. */
+/* Defaults: fp32, query-row mode, null stream, library-managed scratch,
+ * deterministic = 1. */
 void crkv_opts_init(crkv_opts *opts);
 
 /*

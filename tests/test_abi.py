@@ -49,7 +49,7 @@ FAKE = 0x10000   # aligned, never dereferenced: validation fails first
 
 
 def _call(Q=FAKE, K=None, V=None, lens=(64, 64, 16), q_len=16, H=4, H_kv=4, d=64, out=FAKE,
-          impact=FAKE, dtype=crkv.CRKV_F32, mode=0, workspace=None):
+          impact=FAKE, dtype=crkv.CRKV_F32, mode=0, workspace=None, deterministic=1):
     L = crkv.lib()
     m = len(lens) - 1
     K = K if K is not None else [FAKE] * (m + 1)
@@ -62,6 +62,8 @@ def _call(Q=FAKE, K=None, V=None, lens=(64, 64, 16), q_len=16, H=4, H_kv=4, d=64
     o.dtype = dtype
     o.mode = mode
     o.workspace = workspace
+    assert o.deterministic == 1   # the default
+    o.deterministic = deterministic
     rc = L.crkv_attn_chunks(Q, ka, va, la, m, q_len, H, H_kv, d, out, impact, ctypes.byref(o))
     return rc, L.crkv_last_error().decode()
 
@@ -83,6 +85,7 @@ def _call(Q=FAKE, K=None, V=None, lens=(64, 64, 16), q_len=16, H=4, H_kv=4, d=64
     (dict(dtype=7), -1, "dtype"),
     (dict(mode=5), -1, "mode"),
     (dict(workspace=FAKE + 16), -1, "256-byte"),
+    (dict(deterministic=2), -1, "deterministic"),
 ])
 def test_attn_rejects_invalid_arguments(crkv_lib, kwargs, status, needle):
     rc, msg = _call(**kwargs)
