@@ -135,6 +135,132 @@ struct Stager {
     }
 };
 
+// Eight codes (two dwords, lowest byte first) times float32 scales.
+__device__ __forceinline__ void codes_times(uint32_t lo, uint32_t hi, const float *sc, float *x)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = (float)(int)(int8_t)(lo >> (8 * e)) * sc[e];
+        x[4 + e] = (float)(int)(int8_t)(hi >> (8 * e)) * sc[4 + e];
+    }
+}
+
+// Key tiles of segments in the 8-bit format (codes [H_kv][len][D] int8, then
+// float32 scales: [H_kv][D] per channel for K, [H_kv][len] per token for V).
+// Staging widens a tile into the bf16 tiles the matrix cores read:
+//   K: x = code * scale[channel] in float32, stored as the pair hi = bf16(x)
+//      (tile lk) and lo = bf16(x - hi) (tile lkl): Q . hi + Q . lo carries K
+//      to about 17 significant bits, as the impact's tolerance needs;
+//   V: bf16(code * scale[token]), one rounding (P . V is already rounded to
+//      bf16 operands).
+// Thread t < CH moves the 16 codes of chunk t (key t / (D/16), channels
+// 16 (t % (D/16)) ..) of K and, with WITH_V, of V; the tile's scales come
+// with it. A tile descriptor's K (V) pointer is its segment's buffer at code
+// row key0 - seg_lo of KV head 0; the segment's scales start
+// H_kv * seg_len * D bytes into that buffer.
+template <int D, bool WITH_V, int NT>
+struct StagedQ8 {
+    u32x4 kc;
+    f32x4 ks[4];
+    u32x4 vc;
+    float vs;
+};
+
+template <int D, bool WITH_V, int NT>
+struct StagerQ8 {
+    static constexpr int CPR = D / 16;          // 16-byte code chunks per row
+    static constexpr int CH = kKeyTile * CPR;   // code chunks per tile
+    static constexpr int NCH = D / 8;           // 16-byte bf16 chunks per row
+    static constexpr int ROW = 2 * D;
+    static_assert(CH <= NT, "one code chunk per thread");
+    using S = StagedQ8<D, WITH_V, NT>;
+    bool active;
+    int key, c16;
+    uint32_t lk0, lk1, lv0, lv1;   // LDS byte offsets of the chunk's two bf16 halves
+
+    __device__ __forceinline__ explicit StagerQ8(int t)
+    {
+        active = t < CH;
+        key = t / CPR;
+        c16 = t % CPR;
+        const int ch0 = 2 * c16, ch1 = 2 * c16 + 1;
+        lk0 = (uint32_t)(key * ROW + ((ch0 ^ kswz<NCH>(key)) << 4));
+        lk1 = (uint32_t)(key * ROW + ((ch1 ^ kswz<NCH>(key)) << 4));
+        lv0 = (uint32_t)(key * ROW + ((ch0 ^ vswz<NCH>(key)) << 4));
+        lv1 = (uint32_t)(key * ROW + ((ch1 ^ vswz<NCH>(key)) << 4));
+    }
+
+    // Keys past n_valid repeat the last real key (masked later).
+    __device__ __forceinline__ S load(TileSR kt, int kv_head, int H_kv) const
+    {
+        S st;
+        if (!active)
+            return st;
+        const int t0 = kt.key0 - kt.seg_lo;
+        const int row = min(key, kt.n_valid - 1);
+        const size_t head_rows = (size_t)kv_head * kt.seg_len;
+        const size_t to_scales = (size_t)H_kv * kt.seg_len * D - (size_t)t0 * D;
+        const gptr<const unsigned char> kb = reinterpret_cast<gptr<const unsigned char>>(kt.K);
+        st.kc = *reinterpret_cast<gptr<const u32x4>>(kb + (head_rows + row) * D + 16 * c16);
+        const gptr<const f32x4> ksc =
+            reinterpret_cast<gptr<const f32x4>>(kb + to_scales + ((size_t)kv_head * D + 16 * c16) * sizeof(float));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            st.ks[j] = ksc[j];
+        if constexpr (WITH_V) {
+            const gptr<const unsigned char> vb = reinterpret_cast<gptr<const unsigned char>>(kt.V);
+            st.vc = *reinterpret_cast<gptr<const u32x4>>(vb + (head_rows + row) * D + 16 * c16);
+            st.vs = reinterpret_cast<gptr<const float>>(vb + to_scales)[head_rows + t0 + row];
+        }
+        return st;
+    }
+
+    __device__ __forceinline__ void store(const S st, unsigned char *lk, unsigned char *lkl,
+                                          unsigned char *lv) const
+    {
+        if (!active)
+            return;
+        float ksc[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ksc[4 * j + e] = st.ks[j][e];
+        float x[16];
+        codes_times(st.kc[0], st.kc[1], ksc, x);
+        codes_times(st.kc[2], st.kc[3], ksc + 8, x + 8);
+        bf16x8 h0, h1, l0, l1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h0[e] = (__bf16)x[e];
+            h1[e] = (__bf16)x[8 + e];
+            l0[e] = (__bf16)(x[e] - (float)h0[e]);
+            l1[e] = (__bf16)(x[8 + e] - (float)h1[e]);
+        }
+        *reinterpret_cast<bf16x8 *>(lk + lk0) = h0;
+        *reinterpret_cast<bf16x8 *>(lk + lk1) = h1;
+        *reinterpret_cast<bf16x8 *>(lkl + lk0) = l0;
+        *reinterpret_cast<bf16x8 *>(lkl + lk1) = l1;
+        if constexpr (WITH_V) {
+            float vsc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vsc[e] = st.vs;
+            float y[16];
+            codes_times(st.vc[0], st.vc[1], vsc, y);
+            codes_times(st.vc[2], st.vc[3], vsc, y + 8);
+            bf16x8 v0, v1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v0[e] = (__bf16)y[e];
+                v1[e] = (__bf16)y[8 + e];
+            }
+            *reinterpret_cast<bf16x8 *>(lv + lv0) = v0;
+            *reinterpret_cast<bf16x8 *>(lv + lv1) = v1;
+        }
+    }
+};
+
 // S^T of one 16-row tile against the two 16-key subtiles of a key tile.
 // Sweep 1 keeps per (row, lane group) a reference maximum m and
 // l = sum of exp2((s - m) * c) over the keys seen so far, with m <= their

@@ -40,7 +40,7 @@
 
 namespace crkv {
 
-template <int D, int RT, bool CROSS>
+template <int D, int RT, bool CROSS, bool KV8>
 __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnArgs a)
 {
     constexpr int KS = D / 32;                 // MFMA k-steps along d
@@ -49,11 +49,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     constexpr int ROW = 2 * D;                 // LDS bytes per K or V row
     constexpr int TILE = kKeyTile * ROW;       // LDS bytes per K (or V) tile
     static_assert(kKeyTile == 32, "tile geometry");
-    const Stager<NCH, false, kThreads> stg1(threadIdx.x);
-    const Stager<NCH, true, kThreads> stg2(threadIdx.x);
+    // bf16 segments are staged as they are; 8-bit ones are widened on the way
+    // (K into a bf16 hi/lo pair of tiles, V into one bf16 tile)
+    using Stg1 = std::conditional_t<KV8, StagerQ8<D, false, kThreads>, Stager<NCH, false, kThreads>>;
+    using Stg2 = std::conditional_t<KV8, StagerQ8<D, true, kThreads>, Stager<NCH, true, kThreads>>;
+    const Stg1 stg1(threadIdx.x);
+    const Stg2 stg2(threadIdx.x);
 
     __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
     __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];   // K lo (8-bit)
     __shared__ float lds_imp[2][kWaves][kKeyTile];
 
     const int tid = threadIdx.x;
@@ -68,6 +73,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     const int packed_total = G * pr.rows;
     const int t0 = it.tile_begin + wave * RT;
     const int wave_min_pos = pr.pos0 + (t0 * kRowTile) / G;
+    auto stage_load = [&](const auto &stg, TileSR kt) {
+        if constexpr (KV8)
+            return stg.load(kt, it.kv_head, a.H_kv);
+        else
+            return stg.load(kt, it.kv_head);
+    };
+    auto stage_store = [&](const auto &stg, const auto &st, int buf) {
+        if constexpr (KV8)
+            stg.store(st, lds_k[buf], lds_kl[buf], lds_v[buf]);
+        else
+            stg.store(st, lds_k[buf], lds_v[buf]);
+    };
 
     int row_pos[RT];
     bf16x8 qf[RT][KS];
@@ -106,12 +123,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     }
     auto sweep1_tile = [&](TileSR kt, int buf, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        bf16x8 kf[2][KS];
+        bf16x8 kf[2][KS], kfl[KV8 ? 2 : 1][KS];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
                 kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+                if constexpr (KV8)
+                    kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
+            }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -119,6 +139,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             for (int ks = 0; ks < KS; ++ks) {
                 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[rt][ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[rt][ks], s1, 0, 0, 0);
+                if constexpr (KV8) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[0][ks], qf[rt][ks], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[1][ks], qf[rt][ks], s1, 0, 0, 0);
+                }
             }
             if constexpr (MASK) {
                 const int lim = min(kt.n_valid - 1, row_pos[rt] - kt.key0);
@@ -146,12 +170,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     // nothing, when some row needs its maximum taken again (sweep1_tile then
     // redoes the tile exactly).
     auto sweep1_tile_ref = [&](int buf) -> bool {
-        bf16x8 kf[2][KS];
+        bf16x8 kf[2][KS], kfl[KV8 ? 2 : 1][KS];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
                 kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+                if constexpr (KV8)
+                    kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
+            }
         float sum[RT];
         bool big = false;
 #pragma unroll
@@ -161,6 +188,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             for (int ks = 0; ks < KS; ++ks) {
                 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[rt][ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[rt][ks], s1, 0, 0, 0);
+                if constexpr (KV8) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[0][ks], qf[rt][ks], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[1][ks], qf[rt][ks], s1, 0, 0, 0);
+                }
             }
             const float mc = row_m[rt] * c;
             float e[8];
@@ -186,23 +217,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     if (n_kt > 0) {
         TileSR cur = to_sr(desc(0));
         uint32_t nraw = desc(1);
-        stg1.store(stg1.load(cur, it.kv_head), lds_k[0], lds_v[0]);
+        stage_store(stg1, stage_load(stg1, cur), 0);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
             const bool more = tt + 1 < n_kt;
             const TileSR nxt = to_sr(nraw);
             nraw = desc(tt + 2);
-            Staged<NCH, false, kThreads> st;
+            decltype(stage_load(stg1, nxt)) st;
             if (more)
-                st = stg1.load(nxt, it.kv_head);
+                st = stage_load(stg1, nxt);
             const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
             if (need_mask)
                 sweep1_tile(cur, buf, std::true_type{});
             else if (!sweep1_tile_ref(buf))
                 sweep1_tile(cur, buf, std::false_type{});
             if (more)
-                stg1.store(st, lds_k[buf ^ 1], lds_v[buf ^ 1]);
+                stage_store(stg1, st, buf ^ 1);
             __syncthreads();
             cur = nxt;
         }
@@ -238,12 +269,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     // Tiles that need the causal or ragged-tail mask.
     auto sweep2_tile = [&](TileSR kt, int buf, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        bf16x8 kf[2][KS], vf[DT];
+        bf16x8 kf[2][KS], kfl[KV8 ? 2 : 1][KS], vf[DT];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
                 kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+                if constexpr (KV8)
+                    kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
+            }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -261,6 +295,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             for (int ks = 0; ks < KS; ++ks) {
                 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[rt][ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[rt][ks], s1, 0, 0, 0);
+                if constexpr (KV8) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[0][ks], qf[rt][ks], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[1][ks], qf[rt][ks], s1, 0, 0, 0);
+                }
             }
             if constexpr (MASK) {
                 const int lim = min(kt.n_valid - 1, row_pos[rt] - kt.key0);
@@ -312,12 +350,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     // between the vector instructions that turn row tile rt's scores into p
     // (exp, impact sums, bf16 rounding). Every stage is a scheduling region.
     auto sweep2_tile_pipe = [&](TileSR kt, int buf) {
-        bf16x8 kf[2][KS], vf[DT];
+        bf16x8 kf[2][KS], kfl[KV8 ? 2 : 1][KS], vf[DT];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
                 kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+                if constexpr (KV8)
+                    kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
+            }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -333,6 +374,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         for (int ks = 0; ks < KS; ++ks) {
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[0][ks], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[0][ks], s1, 0, 0, 0);
+            if constexpr (KV8) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[0][ks], qf[0][ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[1][ks], qf[0][ks], s1, 0, 0, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 pprev;
@@ -344,6 +389,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                 for (int ks = 0; ks < KS; ++ks) {
                     n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[rt + 1][ks], n0, 0, 0, 0);
                     n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[rt + 1][ks], n1, 0, 0, 0);
+                    if constexpr (KV8) {
+                        n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[0][ks], qf[rt + 1][ks], n0, 0, 0, 0);
+                        n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[1][ks], qf[rt + 1][ks], n1, 0, 0, 0);
+                    }
                 }
             }
             if (rt > 0) {
@@ -370,8 +419,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 pprev[i] = (__bf16)p[i];
-            constexpr int n_mfma_max = 2 * KS + DT;
-            const int n_mfma = (rt + 1 < RT ? 2 * KS : 0) + (rt > 0 ? DT : 0);
+            constexpr int QK = (KV8 ? 4 : 2) * KS;   // score MFMAs of a row tile
+            constexpr int n_mfma_max = QK + DT;
+            const int n_mfma = (rt + 1 < RT ? QK : 0) + (rt > 0 ? DT : 0);
 #pragma unroll
             for (int i = 0; i < n_mfma_max; ++i) {
                 if (i < n_mfma) {
@@ -399,16 +449,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     if (n_kt > 0) {
         TileSR cur = to_sr(desc(0)), prev = cur;
         uint32_t nraw = desc(1);
-        stg2.store(stg2.load(cur, it.kv_head), lds_k[0], lds_v[0]);
+        stage_store(stg2, stage_load(stg2, cur), 0);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
             const bool more = tt + 1 < n_kt;
             const TileSR nxt = to_sr(nraw);
             nraw = desc(tt + 2);
-            Staged<NCH, true, kThreads> st;
+            decltype(stage_load(stg2, nxt)) st;
             if (more)
-                st = stg2.load(nxt, it.kv_head);
+                st = stage_load(stg2, nxt);
             if (tt > 0)
                 flush_impact(tt - 1, prev, buf ^ 1);
             const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
@@ -417,7 +467,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             else
                 sweep2_tile_pipe(cur, buf);
             if (more)
-                stg2.store(st, lds_k[buf ^ 1], lds_v[buf ^ 1]);
+                stage_store(stg2, st, buf ^ 1);
             __syncthreads();
             prev = cur;
             cur = nxt;
@@ -447,16 +497,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, bool KV8>
 static void launch_wave_rt(const AttnArgs &args, int n_items, hipStream_t stream)
 {
     if constexpr (RT <= kWaveMaxRowTilesCross) {
         if (args.cross) {
-            hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, true>), dim3(n_items), dim3(kThreads), 0, stream, args);
+            hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, true, KV8>), dim3(n_items), dim3(kThreads), 0, stream,
+                               args);
             return;
         }
     }
-    hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, false>), dim3(n_items), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, false, KV8>), dim3(n_items), dim3(kThreads), 0, stream, args);
 }
 
 hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream)
@@ -467,18 +518,40 @@ hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_item
         return hipErrorInvalidValue;   // no such build; the planner never asks for it
     if (d == 128) {
         if (rt == 7)
-            launch_wave_rt<128, 7>(args, n_items, stream);
+            launch_wave_rt<128, 7, false>(args, n_items, stream);
         else if (rt == 5)
-            launch_wave_rt<128, 5>(args, n_items, stream);
+            launch_wave_rt<128, 5, false>(args, n_items, stream);
         else
-            launch_wave_rt<128, 4>(args, n_items, stream);
+            launch_wave_rt<128, 4, false>(args, n_items, stream);
     } else {
         if (rt == 7)
-            launch_wave_rt<64, 7>(args, n_items, stream);
+            launch_wave_rt<64, 7, false>(args, n_items, stream);
         else if (rt == 5)
-            launch_wave_rt<64, 5>(args, n_items, stream);
+            launch_wave_rt<64, 5, false>(args, n_items, stream);
         else
-            launch_wave_rt<64, 4>(args, n_items, stream);
+            launch_wave_rt<64, 4, false>(args, n_items, stream);
+    }
+    return hipGetLastError();
+}
+
+// Key tiles in the 8-bit format: the same kernel with K widened into a bf16
+// hi/lo pair and V into bf16 while staging (row tiles per wave: 4 or 5).
+hipError_t launch_attn_q8(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    if (n_items <= 0)
+        return hipSuccess;
+    if (rt != 4 && rt != 5)
+        return hipErrorInvalidValue;   // no such build; the planner never asks for it
+    if (d == 128) {
+        if (rt == 5)
+            launch_wave_rt<128, 5, true>(args, n_items, stream);
+        else
+            launch_wave_rt<128, 4, true>(args, n_items, stream);
+    } else {
+        if (rt == 5)
+            launch_wave_rt<64, 5, true>(args, n_items, stream);
+        else
+            launch_wave_rt<64, 4, true>(args, n_items, stream);
     }
     return hipGetLastError();
 }

@@ -28,6 +28,7 @@
 namespace crkv {
 hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_bf16_pair(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_q8(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_decode_bf16(int d, const DecodeArgs &args, int n_items, int n_pairs, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
@@ -423,14 +424,14 @@ int64_t packed_rows(const crkv_problem &p, int G, int mode)
 // its last row. The choice minimises the modelled sum over all workgroups.
 // CRKV_BF16_KERNEL (wave | pair) and CRKV_ROW_TILES force a built choice
 // (tuning experiments and tests).
-void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, int &kernel, int &rt)
+void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, bool q8, int &kernel, int &rt)
 {
-    const char *ek = getenv("CRKV_BF16_KERNEL");
+    const char *ek = q8 ? "wave" : getenv("CRKV_BF16_KERNEL");   // 8-bit segments: the wave kernel's builds
     const char *er = getenv("CRKV_ROW_TILES");
     const int forced_rt = er ? atoi(er) : 0;
     int64_t best_cost = INT64_MAX;
-    kernel = kBf16Pair;
-    rt = kPairRowTiles[0];
+    kernel = q8 ? kBf16Wave : kBf16Pair;
+    rt = q8 ? kQ8RowTiles[0] : kPairRowTiles[0];
     for (int k = kBf16Wave; k <= kBf16Pair; ++k) {
         if (ek && strcmp(ek, k == kBf16Wave ? "wave" : "pair") != 0)
             continue;
@@ -440,6 +441,8 @@ void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, 
         for (int c = 0; c < 3; ++c) {
             const int r = choices[c];
             if (forced_rt && r != forced_rt)
+                continue;
+            if (q8 && r != kQ8RowTiles[0] && r != kQ8RowTiles[1])
                 continue;
             if (k == kBf16Wave && mode == CRKV_IMPACT_CROSS_DOC && r > kWaveMaxRowTilesCross)
                 continue;
@@ -476,9 +479,10 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
                 const crkv_opts &o)
 {
     const int G = H / H_kv;
-    const bool bf16 = o.dtype == CRKV_BF16;
+    const bool q8 = o.dtype == CRKV_KV_Q8;
+    const bool bf16 = o.dtype == CRKV_BF16 || q8;   // Q and out bf16
     if (bf16)
-        choose_bf16(problems, n_problems, G, o.mode, pl.kernel, pl.rt);
+        choose_bf16(problems, n_problems, G, o.mode, q8, pl.kernel, pl.rt);
     else
         pl.rt = 1;
     const int cap = bf16 ? kWaves * pl.rt : 1;   // row tiles per workgroup
@@ -504,7 +508,7 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
         for (int c = 0; c <= p.m; ++c) {
             const int32_t len = p.chunk_len[c];
             pl.segs.push_back(SegDesc{p.chunk_K[c], p.chunk_V[c], len, start});
-            const size_t esz = o.dtype == CRKV_BF16 ? 2 : 4;
+            const size_t esz = q8 ? 1 : o.dtype == CRKV_BF16 ? 2 : 4;   // 8-bit: code bytes
             for (int32_t t = 0; t < len; t += kKeyTile) {
                 KTile kt;
                 kt.K = static_cast<const unsigned char *>(p.chunk_K[c]) + (size_t)t * d * esz;
@@ -630,7 +634,11 @@ crkv_opts resolve(const crkv_opts *opts)
 int validate_batch(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                    const crkv_opts &o)
 {
-    int rc = check_opts(o);
+    // 8-bit segments (CRKV_KV_Q8) come with bf16 Q and out
+    crkv_opts oc = o;
+    if (oc.dtype == CRKV_KV_Q8)
+        oc.dtype = CRKV_BF16;
+    int rc = check_opts(oc);
     if (rc)
         return rc;
     rc = check_shape(n_problems, H, H_kv, d);
@@ -679,7 +687,8 @@ hipError_t launch_planned(const Plan &pl, int n_problems, int H, int H_kv, int d
     if (o.timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
     if (e == hipSuccess)
-        e = o.dtype != CRKV_BF16      ? launch_attn_f32(d, args, (int)pl.items.size(), stream)
+        e = o.dtype == CRKV_KV_Q8    ? launch_attn_q8(d, pl.rt, args, (int)pl.items.size(), stream)
+            : o.dtype != CRKV_BF16   ? launch_attn_f32(d, args, (int)pl.items.size(), stream)
             : pl.kernel == kBf16Wave ? launch_attn_bf16_wave(d, pl.rt, args, (int)pl.items.size(), stream)
                                      : launch_attn_bf16_pair(d, pl.rt, args, (int)pl.items.size(), stream);
     if (e == hipSuccess && o.timing_events[1])
@@ -1185,7 +1194,8 @@ int plan_launch(const crkv_plan *p, void *stream_ptr, void *const *timing_events
     if (timing_events && timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[0]), stream);
     if (e == hipSuccess)
-        e = p->dtype != CRKV_BF16        ? launch_attn_f32(p->d, p->args, p->n_items, stream)
+        e = p->dtype == CRKV_KV_Q8   ? launch_attn_q8(p->d, p->rt, p->args, p->n_items, stream)
+            : p->dtype != CRKV_BF16  ? launch_attn_f32(p->d, p->args, p->n_items, stream)
             : p->kernel == kBf16Wave ? launch_attn_bf16_wave(p->d, p->rt, p->args, p->n_items, stream)
                                      : launch_attn_bf16_pair(p->d, p->rt, p->args, p->n_items, stream);
     if (e == hipSuccess && timing_events && timing_events[1])
@@ -1467,7 +1477,7 @@ int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv
         return rc;
     Plan pl;
     build_plan(pl, problems, n_problems, H, H_kv, d, o);
-    *kernel = o.dtype != CRKV_BF16 ? 0 : pl.kernel == kBf16Wave ? 1 : 2;
+    *kernel = (o.dtype != CRKV_BF16 && o.dtype != CRKV_KV_Q8) ? 0 : pl.kernel == kBf16Wave ? 1 : 2;
     *row_tiles = pl.rt;
     *workgroups = (int)pl.items.size();
     return CRKV_OK;

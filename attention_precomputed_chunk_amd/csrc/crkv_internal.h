@@ -22,6 +22,7 @@ enum Bf16Kernel { kBf16Wave = 0, kBf16Pair = 1 };
 constexpr int kWaveRowTiles[3] = {4, 5, 7};     // rt the wave kernels are built for
 constexpr int kWaveMaxRowTilesCross = 5;        // cross-document wave kernels: 7 would spill
 constexpr int kPairRowTiles[3] = {2, 4, 6};     // rt the pair kernels are built for
+constexpr int kQ8RowTiles[2] = {4, 5};          // rt of the wave kernel's 8-bit builds
 // Planner cost model, SIMD cycles per 32-key step of one workgroup: a fixed
 // part and a part per row tile (fitted to measurements on MI355X; the wave
 // kernel's per-tile part scaled by its measured 9 % gain from the pipelined

@@ -62,6 +62,9 @@ SELECT_CONFIGS = {"llama3_8b_select_kv_32l": "llama3_8b_gqa_32l"}
 METRIC_ROPE = "re-positioned key-layers/s (rotary shift of cached keys); % of HBM roofline"
 ROPE_CONFIGS = {"llama3_8b_rope_shift_32l": "llama3_8b_gqa_32l"}
 Q8_CONFIGS = {"llama3_8b_decode_q8_32l": "llama3_8b_decode_32l"}
+# the prefill over the same workload's cache stored in the 8-bit format
+# (quantised once before timing)
+Q8_ATTN_CONFIGS = {"llama3_8b_gqa_32l_q8": "llama3_8b_gqa_32l"}
 SMALL_CONFIGS = ("tiny", "llama2_7b_layer")
 DEFAULT_CONFIG = "llama3_8b_gqa_32l"
 # timed after the headline in the default run and reported under "configs"
@@ -194,6 +197,25 @@ def cpu_baseline(wl, budget_s=15.0):
         oracle.run_workload(wl, problems=[0], n_threads=1)
         rec["single_thread_value"] = wl.problems[0].n_keys / (time.perf_counter() - t0)
     return rec
+
+
+def cpu_baseline_q8(wl, budget_s=15.0):
+    """The oracle of the 8-bit prefill (quantise, dequantise, fp64 attention)
+    on the first layers of the workload, every host core."""
+    import oracle
+    from oracle import q8
+    t0 = time.perf_counter()
+    done = 0
+    for p in wl.problems:
+        q8.attn(p, wl.H, wl.H_kv, wl.d, wl.mode)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": sum(p.n_keys for p in wl.problems[:done]) / el, "unit": "KV tokens/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "layers 0..%d of %d (quantise + dequantise + fp64 attention), %.1f s"
+            % (done - 1, len(wl.problems), el)}
 
 
 def bench_q8_decode(args, torch, crkv, workloads):
@@ -505,9 +527,13 @@ def main():
 def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu):
     """Attention + impact combine + top-k of one workload: `steps` timed
     steps after `warmup`, the attention kernel bracketed by HIP events on the
-    library's launch stream; returns the record (not printed)."""
-    log("generating %s" % name)
-    wl = workloads.generate(name)
+    library's launch stream; returns the record (not printed). For an 8-bit
+    workload the segments are quantised by the library once, before timing,
+    and the attention reads the codes."""
+    q8 = name in Q8_ATTN_CONFIGS
+    base = Q8_ATTN_CONFIGS.get(name, name)
+    log("generating %s" % base)
+    wl = workloads.generate(base)
     dev = "cuda:0"
 
     def up(a):
@@ -525,12 +551,32 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
     idx = [torch.empty(k, dtype=torch.int32, device=dev) for k in ks]
     ns = [p.n_doc for p in wl.problems]
     imps = [pr["impact"] for pr in problems]
+    dtype = crkv.CRKV_KV_Q8 if q8 else None
+    q8_bytes = 0
+    if q8:   # the stored cache: every segment quantised once, the bf16 copies dropped
+        segs = []
+        for pr, p in zip(problems, wl.problems):
+            kq, vq = [], []
+            for k, v, n in zip(pr["chunk_K"], pr["chunk_V"], p.lens):
+                nk = crkv.crkv_q8_bytes(wl.H_kv, n, wl.d, crkv.CRKV_Q8_K)
+                nv = crkv.crkv_q8_bytes(wl.H_kv, n, wl.d, crkv.CRKV_Q8_V)
+                q8_bytes += nk + nv
+                bk = torch.empty(max(nk, 16), dtype=torch.uint8, device=dev)
+                bv = torch.empty(max(nv, 16), dtype=torch.uint8, device=dev)
+                segs += [(k, bk, n, crkv.CRKV_Q8_K), (v, bv, n, crkv.CRKV_Q8_V)]
+                kq.append(bk)
+                vq.append(bv)
+            pr["chunk_K"], pr["chunk_V"] = kq, vq
+        crkv.crkv_quantize_q8(segs, wl.H_kv, wl.d)
+        torch.cuda.synchronize()
+        del segs
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
 
     if wl.spec.decode:
         plan = {"kernel": "decode_split+merge", "row_tiles": 1, "workgroups": None}
     else:
-        plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+        plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode, dtype=dtype)
     log("plan: %s" % plan)
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
@@ -543,7 +589,7 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
             crkv.crkv_decode_chunks_batched(batch, wl.H, wl.H_kv, wl.d, timing_events=events)
             return
         crkv.crkv_attn_chunks_batched(batch, wl.H, wl.H_kv, wl.d, mode=wl.mode,
-                                      timing_events=events)
+                                      timing_events=events, dtype=dtype)
         crkv.crkv_topk_batched(imps, ns, ks, idx)
 
     log("warmup %d" % warmup)
@@ -565,6 +611,8 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
     tokens = workloads.kv_tokens(wl)
     value = tokens / (wall / steps)
     nbytes, flops, npairs = algorithmic_work(wl)
+    if q8:   # the codes and scales replace the bf16 K/V bytes
+        nbytes += q8_bytes - sum(p.n_keys * 2 * wl.H_kv * wl.d * 2 for p in wl.problems)
     k_ms = float(np.mean(kern_ms))
     achieved_gbs = nbytes / (k_ms * 1e-3) / 1e9
     achieved_tf = flops / (k_ms * 1e-3) / 1e12
@@ -588,6 +636,9 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
     spec = wl.spec
     cfg = {"workload": name, "problems": len(wl.problems), "H": wl.H, "H_kv": wl.H_kv,
            "d": wl.d, "mode": wl.mode, "r": wl.r}
+    if q8:
+        cfg["kv_format"] = ("int8 codes; fp32 scales per (KV head, channel) for K, per (KV head, token) for V; "
+                            "quantised once before timing")
     if spec.chunk_lens:
         cfg.update({"chunks": len(spec.chunk_lens), "chunk_len": spec.chunk_lens[0],
                     "q_len": spec.q_len, "n_doc": int(sum(spec.chunk_lens))})
@@ -604,20 +655,20 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
            "data": "synthetic", "config": cfg, "roofline": primary, "roofline_other": secondary,
            "kv_tokens_per_step": tokens}
     if not decode:
-        rec["graph"] = graph_replay(steps, warmup, torch, crkv, wl, problems, ks, idx, tokens)
+        rec["graph"] = graph_replay(steps, warmup, torch, crkv, wl, problems, ks, idx, tokens, dtype)
     if with_cpu:
         log("cpu baseline (oracle)")
-        rec["cpu_baseline"] = cpu_baseline(wl)
+        rec["cpu_baseline"] = cpu_baseline_q8(wl) if q8 else cpu_baseline(wl)
     del problems, batch, imps
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec
 
 
-def graph_replay(steps, warmup, torch, crkv, wl, problems, ks, idx, tokens):
+def graph_replay(steps, warmup, torch, crkv, wl, problems, ks, idx, tokens, dtype=None):
     """The step (attention + impact combine + top-k) planned once and captured
     into a graph; W replays untimed, then K timed between synchronisations."""
-    plan = crkv.Plan(problems, wl.H, wl.H_kv, wl.d, ks=ks, idxs=idx, mode=wl.mode)
+    plan = crkv.Plan(problems, wl.H, wl.H_kv, wl.d, ks=ks, idxs=idx, mode=wl.mode, dtype=dtype)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):

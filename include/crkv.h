@@ -62,9 +62,11 @@ typedef enum {
     CRKV_E_NOMEM = -4        /* device or pinned host allocation failed      */
 } crkv_status;
 
-/* CRKV_KV_Q8: K/V segments in the 8-bit format of crkv_quantize_q8, Q and
- * out bf16; accepted by crkv_decode_chunks_batched (and its workspace size)
- * only, every other entry point returns CRKV_E_UNSUPPORTED or CRKV_E_INVAL. */
+/* CRKV_KV_Q8: K/V segments in the 8-bit format of crkv_quantize_q8 (every
+ * segment, documents and the query block's own), Q and out bf16; accepted by
+ * the attention entry points (crkv_attn_chunks[_batched][_static], the plan
+ * and size functions) and by crkv_decode_chunks_batched; the gather/scatter,
+ * rotation and quantise entry points refuse it. */
 typedef enum { CRKV_F32 = 0, CRKV_BF16 = 1, CRKV_KV_Q8 = 2 } crkv_dtype;
 
 /*
@@ -148,7 +150,14 @@ typedef struct crkv_problem {
 } crkv_problem;
 
 /* All problems of a batch (shared H, H_kv, d, dtype and mode; each with its
- * own chunks, lengths and q_len) in one attention launch. */
+ * own chunks, lengths and q_len) in one attention launch.
+ * With opts->dtype == CRKV_KV_Q8 every chunk_K[c] / chunk_V[c] is a buffer in
+ * the 8-bit format of crkv_quantize_q8 (kinds CRKV_Q8_K and CRKV_Q8_V,
+ * 16-byte aligned) for chunk_len[c] keys, and Q and out are bf16. The call is
+ * the attention over the dequantised cache (code * scale): key tiles are
+ * widened to bf16 while they are staged, K as a hi/lo pair of bf16 values
+ * (Q . K carried to about 17 significant bits, for the impact) and V with its
+ * token scale applied and rounded once to bf16. */
 int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv,
                              int d, const crkv_opts *opts);
 

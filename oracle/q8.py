@@ -33,7 +33,8 @@ K or [H_kv][len] for V. A segment with len = 0 occupies no bytes.
 A decode step over quantised segments is the decode step (the newest token's
 row over every cached key, TurboRAG summary's generation loop) over the
 dequantised cache: ``decode`` builds the dequantised segments in float64 and
-runs the fp64 attention oracle on them.
+runs the fp64 attention oracle on them; ``attn`` does the same for the
+prefill (query rows, impact and the other modes).
 """
 from __future__ import annotations
 
@@ -124,6 +125,17 @@ def quantize_problem(problem, dtype: str = "bf16"):
     kq = [quantize(k, "k", dtype) for k in problem.K]
     vq = [quantize(v, "v", dtype) for v in problem.V]
     return kq, vq
+
+
+def attn(problem, H: int, H_kv: int, d: int, mode: str, kq=None, vq=None):
+    """(out, impact, lse=None) of the attention in any mode (query rows,
+    cross-document, all rows) over the quantised cache: the fp64 attention
+    oracle on the dequantised segments, Q widened exactly from bf16."""
+    import oracle
+    if kq is None or vq is None:
+        kq, vq = quantize_problem(problem)
+    dp = DequantProblem(problem, kq, vq)
+    return oracle.attn(dp, H, H_kv, d, "f64", mode)
 
 
 def decode(problem, H: int, H_kv: int, d: int, kq=None, vq=None):

@@ -29,6 +29,7 @@ struct ProbDesc;
 }
 hipError_t launch_attn_bf16_wave(int, int, const AttnArgs &, int, hipStream_t) { launched("wave"); }
 hipError_t launch_attn_bf16_pair(int, int, const AttnArgs &, int, hipStream_t) { launched("pair"); }
+hipError_t launch_attn_q8(int, int, const AttnArgs &, int, hipStream_t) { launched("q8 attention"); }
 hipError_t launch_decode_bf16(int, const DecodeArgs &, int, int, hipStream_t) { launched("decode"); }
 hipError_t launch_attn_f32(int, const AttnArgs &, int, hipStream_t) { launched("f32"); }
 hipError_t launch_combine(const ProbDesc *, int, int, hipStream_t) { launched("combine"); }
@@ -102,8 +103,9 @@ static void plan_round_trip(const std::vector<FakeProblem *> &ps, int H, int H_k
     crkv_opts o = opts(dtype, mode);
     int kernel = -1, rt = -1, wg = -1;
     EXPECT(crkv_plan_info(arr.data(), (int)arr.size(), H, H_kv, d, &o, &kernel, &rt, &wg) == CRKV_OK);
-    EXPECT(kernel == (dtype == CRKV_BF16 ? kernel : 0));
+    EXPECT(dtype != CRKV_F32 || kernel == 0);
     EXPECT(dtype != CRKV_BF16 || kernel == 1 || kernel == 2);
+    EXPECT(dtype != CRKV_KV_Q8 || (kernel == 1 && (rt == 4 || rt == 5)));
     EXPECT(rt >= 1 && wg >= 1);
     EXPECT(crkv_workspace_size(arr.data(), (int)arr.size(), H, H_kv, d, &o) > 0);
     if (dtype == CRKV_BF16 && mode == CRKV_IMPACT_QUERY_ROWS) {
@@ -165,8 +167,8 @@ int main()
         bad.workspace = fake(50) + 16;
         EXPECT(call(p.c(), 4, 4, 64, bad) == CRKV_E_INVAL);
         bad = o;
-        bad.dtype = CRKV_KV_Q8;
-        EXPECT(call(p.c(), 4, 4, 64, bad) != CRKV_OK);
+        bad.dtype = 9;
+        EXPECT(call(p.c(), 4, 4, 64, bad) == CRKV_E_INVAL);
         EXPECT(crkv_attn_chunks_batched(nullptr, 0, 4, 4, 64, &o) == CRKV_E_INVAL);
         EXPECT(crkv_attn_chunks_batched(nullptr, 1, 4, 4, 64, &o) == CRKV_E_INVAL);
         // static-scratch entry point: a caller workspace, and a batch too large
@@ -235,6 +237,8 @@ int main()
         FakeProblem cd(std::vector<int>(8, 1024), 128);
         plan_round_trip({&cd}, 32, 32, 128, CRKV_BF16, CRKV_IMPACT_CROSS_DOC);
         plan_round_trip({&cd}, 32, 32, 128, CRKV_BF16, CRKV_IMPACT_ALL_ROWS);
+        plan_round_trip(l3p, 32, 8, 128, CRKV_KV_Q8, CRKV_IMPACT_QUERY_ROWS);   // 8-bit segments
+        plan_round_trip({&cd}, 32, 32, 128, CRKV_KV_Q8, CRKV_IMPACT_CROSS_DOC);
         std::vector<FakeProblem> rg;
         unsigned s = 7;
         auto rnd = [&](int lo, int hi) {

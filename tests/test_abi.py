@@ -275,18 +275,24 @@ def test_quantize_q8_rejects_invalid_arguments(crkv_lib):
     assert L.crkv_q8_bytes(8, 5, 64, 7) == 0
 
 
-def test_q8_dtype_is_decode_only(crkv_lib):
-    """CRKV_KV_Q8 passes the decode step's validation (the workspace size is
-    computed) and is refused by the prefill entry points."""
+def test_q8_dtype_in_attention_and_decode(crkv_lib):
+    """CRKV_KV_Q8 passes the decode step's and the prefill's validation (the
+    workspace sizes are computed, the planner picks an 8-bit build of the
+    wave kernel) and is refused by the entry points that move or rotate
+    bf16 rows."""
     p = dict(Q=FAKE, chunk_K=[FAKE, FAKE], chunk_V=[FAKE, FAKE], chunk_len=[64, 3], q_len=1,
              out=FAKE, impact=FAKE)
     assert crkv.crkv_decode_workspace_size([p], 8, 2, 128, dtype=crkv.CRKV_KV_Q8) > 0
-    with pytest.raises(crkv.CrkvError) as e:
-        crkv.crkv_attn_chunks_batched([p], 8, 2, 128, dtype=crkv.CRKV_KV_Q8)
-    assert e.value.status == -1
+    for mode in ("query", "cross", "all"):
+        assert crkv.crkv_workspace_size([p], 8, 2, 128, mode=mode, dtype=crkv.CRKV_KV_Q8) > 0
+        plan = crkv.crkv_plan_info([p], 8, 2, 128, mode=mode, dtype=crkv.CRKV_KV_Q8)
+        assert plan["kernel"] == "bf16_wave" and plan["row_tiles"] in (4, 5), plan
     with pytest.raises(crkv.CrkvError) as e:
         crkv.crkv_decode_chunks_batched([p], 8, 2, 128, dtype=5)
     assert e.value.status == -2
+    with pytest.raises(crkv.CrkvError) as e:
+        crkv.crkv_rope_shift([(FAKE, 64, 3)], 2, 128, crkv.CRKV_KV_Q8)
+    assert e.value.status == -1
 
 
 def test_plan_create_rejects_invalid_arguments(crkv_lib):
@@ -306,7 +312,7 @@ def test_plan_create_rejects_invalid_arguments(crkv_lib):
     idx = (ctypes.c_void_p * 1)(FAKE)
     k[0] = 65                                                                                       # k > N_doc
     assert L.crkv_plan_create(arr, 1, 8, 2, 128, k, idx, ctypes.byref(o), ctypes.byref(h)) == -1
-    o.dtype = crkv.CRKV_KV_Q8
+    o.dtype = 9
     k[0] = 6
     assert L.crkv_plan_create(arr, 1, 8, 2, 128, k, idx, ctypes.byref(o), ctypes.byref(h)) == -1
     assert h.value is None

@@ -175,6 +175,50 @@ def test_decode_over_an_exactly_stored_cache():
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("mode", ["query", "cross", "all"])
+def test_attention_over_an_exactly_stored_cache(mode):
+    """The same exactly stored cache (integer K with a 127 token, V in
+    sixteenths): the prefill over the format (out, impact, every mode)
+    equals the prefill over the original bf16 values."""
+    wl = workloads.custom(6, [37, 0, 1, 50], 9, 4, 2, 64, dtype="bf16", mode=mode)
+    p = wl.problems[0]
+    rng = np.random.default_rng(10)
+    for i, s in enumerate(p.K):
+        v = rng.integers(-127, 128, size=s.shape).astype(np.float32)
+        if v.size:
+            v[:, 0, :] = 127.0
+        p.K[i] = f32_to_bf16_bits(v / np.float32(64.0))   # scale 1/64: scores of moderate size
+    for i, s in enumerate(p.V):
+        v = rng.integers(-127, 128, size=s.shape).astype(np.float32)
+        if v.size:
+            v[..., 0] = 127.0
+        p.V[i] = f32_to_bf16_bits(v / np.float32(16.0))
+    kq, vq = q8.quantize_problem(p)
+    for (c, s), k in zip(kq, p.K):
+        assert np.array_equal(q8.dequantize(c, s, "k"), workloads.widen(k, "bf16"))
+    out_ref, imp_ref, _ = oracle.attn(p, wl.H, wl.H_kv, wl.d, "bf16", mode)
+    out, imp, _ = q8.attn(p, wl.H, wl.H_kv, wl.d, mode, kq, vq)
+    np.testing.assert_allclose(out, out_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(imp, imp_ref, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_over_quantised_cache_is_attention_over_dequantised_values():
+    """An ordinary (inexact) cache: the prefill over the format equals the fp64
+    attention over code * scale built here by hand, and the impact still sums
+    to q_len * H."""
+    wl = workloads.custom(7, [70, 33], 12, 4, 2, 64, dtype="bf16", k_outliers=2)
+    p = wl.problems[0]
+    kq, vq = q8.quantize_problem(p)
+    Ks = [c.astype(np.float64) * s[:, None, :].astype(np.float64) for c, s in kq]
+    Vs = [c.astype(np.float64) * s[:, :, None].astype(np.float64) for c, s in vq]
+    hand = workloads.Problem(K=Ks, V=Vs, lens=list(p.lens), q_len=p.q_len, Q=workloads.widen(p.Q, "bf16"))
+    out_ref, imp_ref, _ = oracle.attn(hand, wl.H, wl.H_kv, wl.d, "f64", "query")
+    out, imp, _ = q8.attn(p, wl.H, wl.H_kv, wl.d, "query")
+    np.testing.assert_array_equal(out, out_ref)
+    np.testing.assert_array_equal(imp, imp_ref)
+    assert abs(imp.sum() - p.q_len * wl.H) < 1e-9
+
+
 @pytest.mark.parametrize("mutant", ["half_away", "scale_128", "no_float32_quotient", "wrong_axis"])
 def test_pins_catch_planted_mistakes(mutant, monkeypatch):
     real = q8.quantize
