@@ -14,13 +14,13 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcrkv.so")
-SOURCES = ["crkv_api.hip", "attn_bf16_wave.hip", "attn_bf16_pair.hip", "decode_bf16.hip", "attn_f32.hip",
+SOURCES = ["crkv_api.hip", "attn_bf16_wave.hip", "attn_lse.hip", "attn_bf16_pair.hip", "decode_bf16.hip", "attn_f32.hip",
            "topk.hip", "kvsel.hip", "rope.hip", "q8.hip"]
 # Device-code files. They never meet a NaN on the contract's inputs (masked
 # scores are -inf), so maxima need no NaN canonicalisation; and matrix-core
 # results are kept in ordinary VGPRs, which the vector ALU reads directly
 # (the default AGPR form costs a v_accvgpr_read per score).
-KERNEL_SOURCES = {"attn_bf16_wave.hip", "attn_bf16_pair.hip", "decode_bf16.hip", "attn_f32.hip", "topk.hip",
+KERNEL_SOURCES = {"attn_bf16_wave.hip", "attn_lse.hip", "attn_bf16_pair.hip", "decode_bf16.hip", "attn_f32.hip", "topk.hip",
                   "kvsel.hip", "rope.hip", "q8.hip"}
 KERNEL_FLAGS = ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 ARCH = os.environ.get("CRKV_OFFLOAD_ARCH", "gfx950")

@@ -40,9 +40,11 @@
 
 namespace crkv {
 
-template <int D, int RT, bool CROSS, bool KV8>
+template <int D, int RT, bool CROSS, bool KV8, bool LSE_IN>
 __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnArgs a)
 {
+    constexpr int NT = kThreads;
+    constexpr int NW = kWaves;
     constexpr int KS = D / 32;                 // MFMA k-steps along d
     constexpr int DT = D / 16;                 // output d tiles
     constexpr int NCH = D / 8;                 // 16-byte chunks per row
@@ -51,15 +53,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     static_assert(kKeyTile == 32, "tile geometry");
     // bf16 segments are staged as they are; 8-bit ones are widened on the way
     // (K into a bf16 hi/lo pair of tiles, V into one bf16 tile)
-    using Stg1 = std::conditional_t<KV8, StagerQ8<D, false, kThreads>, Stager<NCH, false, kThreads>>;
-    using Stg2 = std::conditional_t<KV8, StagerQ8<D, true, kThreads>, Stager<NCH, true, kThreads>>;
+    using Stg1 = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
+    using Stg2 = std::conditional_t<KV8, StagerQ8<D, true, NT>, Stager<NCH, true, NT>>;
     const Stg1 stg1(threadIdx.x);
     const Stg2 stg2(threadIdx.x);
 
     __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
     __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE];
     __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];   // K lo (8-bit)
-    __shared__ float lds_imp[2][kWaves][kKeyTile];
+    __shared__ float lds_imp[2][NW][kKeyTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -214,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     // Descriptors are loaded two tiles ahead of use and data one tile ahead;
     // a descriptor reaches scalar registers one iteration after its load.
     auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
-    if (n_kt > 0) {
+    if (!LSE_IN && n_kt > 0) {
         TileSR cur = to_sr(desc(0));
         uint32_t nraw = desc(1);
         stage_store(stg1, stage_load(stg1, cur), 0);
@@ -241,13 +243,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
 
     // Combine the four lane groups of each row into its log2-domain lse;
     // padded rows get +inf so every weight they would produce is 0.
+    // (or read them: with LSE_IN, pass 1 ran as attn_lse_kernel on the same items)
     float lse2[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        float m = row_m[rt], l = row_l[rt];
-        merge_state(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16), c);
-        merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32), c);
-        lse2[rt] = (row_pos[rt] < 0x3fffffff) ? m * c + __log2f(l) : INFINITY;
+        if constexpr (LSE_IN) {
+            // pass 1 writes the item's real row tiles only; padded rows get +inf here
+            lse2[rt] = (row_pos[rt] < 0x3fffffff)
+                           ? as_global(a.lse)[(size_t)blockIdx.x * a.lse_stride + (wave * RT + rt) * kRowTile + li]
+                           : INFINITY;
+        } else {
+            float m = row_m[rt], l = row_l[rt];
+            merge_state(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16), c);
+            merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32), c);
+            lse2[rt] = (row_pos[rt] < 0x3fffffff) ? m * c + __log2f(l) : INFINITY;
+        }
     }
 
     // ---------------------------------------------------------------- sweep 2: P.V and impact
@@ -260,10 +270,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
 
     const gptr<float> partial = as_global(pr.partial) + (size_t)it.slot * pr.n_keys;
     auto flush_impact = [&](int tt, TileSR kt, int buf) {
-        if (wave == (tt & 3)) {
-            if (lane < kt.n_valid)
-                partial[kt.key0 + lane] = lds_imp[buf][0][lane] + lds_imp[buf][1][lane] +
-                                          lds_imp[buf][2][lane] + lds_imp[buf][3][lane];
+        if (wave == tt % NW) {
+            if (lane < kt.n_valid) {
+                float sum = lds_imp[buf][0][lane];
+#pragma unroll
+                for (int w = 1; w < NW; ++w)
+                    sum += lds_imp[buf][w][lane];
+                partial[kt.key0 + lane] = sum;
+            }
         }
     };
     // Tiles that need the causal or ragged-tail mask.
@@ -497,17 +511,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     }
 }
 
-template <int D, int RT, bool KV8>
-static void launch_wave_rt(const AttnArgs &args, int n_items, hipStream_t stream)
+template <int D, int RT, bool KV8, bool LSE_IN>
+static void launch_wave_rt2(const AttnArgs &args, int n_items, hipStream_t stream)
 {
     if constexpr (RT <= kWaveMaxRowTilesCross) {
         if (args.cross) {
-            hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, true, KV8>), dim3(n_items), dim3(kThreads), 0, stream,
-                               args);
+            hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, true, KV8, LSE_IN>), dim3(n_items), dim3(kThreads), 0,
+                               stream, args);
             return;
         }
     }
-    hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, false, KV8>), dim3(n_items), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_bf16_wave_kernel<D, RT, false, KV8, LSE_IN>), dim3(n_items), dim3(kThreads), 0, stream,
+                       args);
+}
+
+// args.lse non-null: pass 1 already ran (attn_lse_kernel) and pass 2 reads it.
+template <int D, int RT, bool KV8>
+static void launch_wave_rt(const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    if (args.lse)
+        launch_wave_rt2<D, RT, KV8, true>(args, n_items, stream);
+    else
+        launch_wave_rt2<D, RT, KV8, false>(args, n_items, stream);
 }
 
 hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream)

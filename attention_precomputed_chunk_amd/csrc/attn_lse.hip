@@ -1,0 +1,245 @@
+// Pass 1 of the attention (the row log-sum-exp) as a kernel of its own, for
+// gfx950 (CDNA4), run before the one-wave kernel's pass 2 on the same work
+// items (TurboRAG summary, the causal attention equation; CacheBlend
+// summary, the selective-recompute listing's softmax over every key):
+//   lse_j = log sum_i exp(q_j . k_i / sqrt(d))   over the keys visible to row j
+// stored in the log2 domain (lse_j / ln 2) per packed row of each item.
+//
+// Why a separate kernel: a wave issues its vector and matrix instructions in
+// order, and in the one-wave-per-SIMD kernel the two barely overlap; a second
+// wave on the SIMD supplies the overlap. Pass 2 needs the output accumulators
+// of all its rows and so fills a SIMD's registers with one wave, but pass 1
+// needs only Q and two numbers per row: here 8 waves (two per SIMD) share
+// each staged K tile, and an item's row tiles are dealt to them round robin
+// (wave w takes tiles w, w + 8, ...). Each wave runs a body compiled for its
+// own number of row tiles (0 .. 4), so no padded tile is computed; every body
+// meets the same barriers.
+//
+// The arithmetic per key tile is the one-wave kernel's pass 1: scores on the
+// matrix cores (S^T = K Q^T, layout in attn_bf16_common.h), the running
+// maximum and sum of exp2 per row, with unmasked tiles summed against a
+// reference maximum and the exact maximum taken again only when a sum leaves
+// float32's comfortable range (see kLseRescaleBound).
+#include <type_traits>
+
+#include "attn_bf16_common.h"
+
+namespace crkv {
+
+template <int D, int R, bool KV8, typename Stg>
+__device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr, const Stg &stg,
+                                         unsigned char (*lds_k)[kKeyTile * 2 * D],
+                                         unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int wave, int lane)
+{
+    constexpr int KS = D / 32;
+    constexpr int NCH = D / 8;
+    constexpr int ROW = 2 * D;
+    constexpr int RR = R > 0 ? R : 1;
+    const int li = lane & 15, lg = lane >> 4;
+    const int G = a.G;
+    const float c = a.c_log2;
+    const int n_kt = it.n_ktiles;
+
+    int row_pos[RR];
+    bf16x8 qf[RR][KS];
+    float row_m[RR], row_l[RR];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        load_q_rows<KS>(pr, it, G, it.tile_begin + wave + i * kLseWaves, li, lg, qf[i], row_pos[i]);
+        row_m[i] = -INFINITY;
+        row_l[i] = 0.f;
+    }
+    const int wave_min_pos = pr.pos0 + ((it.tile_begin + wave) * kRowTile) / G;
+
+    const int kkey0 = 8 * (li >> 2) + (li & 3);
+    const int ksw = kswz<NCH>(kkey0);
+    auto k_off = [&](int sub, int ks) { return (kkey0 + 4 * sub) * ROW + (((4 * ks + lg) ^ ksw) << 4); };
+    auto load_kf = [&](int buf, bf16x8 (&kf)[2][KS], bf16x8 (&kfl)[KV8 ? 2 : 1][KS]) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][k_off(sub, ks)]);
+                if constexpr (KV8)
+                    kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
+            }
+    };
+    auto qk = [&](const bf16x8 (&kf)[2][KS], const bf16x8 (&kfl)[KV8 ? 2 : 1][KS], int i, f32x4 &s0, f32x4 &s1) {
+        s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[i][ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf[i][ks], s1, 0, 0, 0);
+            if constexpr (KV8) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[0][ks], qf[i][ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[1][ks], qf[i][ks], s1, 0, 0, 0);
+            }
+        }
+    };
+    // Exact running maximum and rescaled sum (masked tiles, a row's first
+    // tile, and the fallback of the reference path).
+    auto tile_exact = [&](TileSR kt, int buf, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        bf16x8 kf[2][KS], kfl[KV8 ? 2 : 1][KS];
+        load_kf(buf, kf, kfl);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            f32x4 s0, s1;
+            qk(kf, kfl, i, s0, s1);
+            if constexpr (MASK) {
+                const int lim = min(kt.n_valid - 1, row_pos[i] - kt.key0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (8 * lg + e > lim)
+                        s0[e] = -INFINITY;
+                    if (8 * lg + 4 + e > lim)
+                        s1[e] = -INFINITY;
+                }
+            }
+            const float tmax = fmaxf(fmaxf(fmaxf(row_m[i], s0[0]), fmaxf(s0[1], s0[2])),
+                                     fmaxf(fmaxf(s0[3], s1[0]), fmaxf(fmaxf(s1[1], s1[2]), s1[3])));
+            const float mc = ((tmax == -INFINITY) ? 0.f : tmax) * c;
+            float sum = exp2_hw(__builtin_fmaf(s0[0], c, -mc)) + exp2_hw(__builtin_fmaf(s1[0], c, -mc));
+#pragma unroll
+            for (int e = 1; e < 4; ++e)
+                sum += exp2_hw(__builtin_fmaf(s0[e], c, -mc)) + exp2_hw(__builtin_fmaf(s1[e], c, -mc));
+            row_l[i] = __builtin_fmaf(row_l[i], exp2_hw(__builtin_fmaf(row_m[i], c, -mc)), sum);
+            row_m[i] = tmax;
+        }
+    };
+    // Unmasked tile against the current maxima; false (nothing changed) when
+    // some row needs its maximum taken again.
+    auto tile_ref = [&](int buf) -> bool {
+        bf16x8 kf[2][KS], kfl[KV8 ? 2 : 1][KS];
+        load_kf(buf, kf, kfl);
+        float sum[RR];
+        bool big = false;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            f32x4 s0, s1;
+            qk(kf, kfl, i, s0, s1);
+            const float mc = row_m[i] * c;
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                e[j] = exp2_hw(__builtin_fmaf(s0[j], c, -mc));
+                e[4 + j] = exp2_hw(__builtin_fmaf(s1[j], c, -mc));
+            }
+            sum[i] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            big |= sum[i] > kLseRescaleBound;
+        }
+        if (__builtin_amdgcn_ballot_w64(big))
+            return false;
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            row_l[i] += sum[i];
+        return true;
+    };
+
+    auto stage_load = [&](TileSR kt) {
+        if constexpr (KV8)
+            return stg.load(kt, it.kv_head, a.H_kv);
+        else
+            return stg.load(kt, it.kv_head);
+    };
+    auto stage_store = [&](const auto &st, int buf) {
+        if constexpr (KV8)
+            stg.store(st, lds_k[buf], lds_kl[buf], nullptr);
+        else
+            stg.store(st, lds_k[buf], nullptr);
+    };
+    // Descriptors two tiles ahead, data one tile ahead, K double-buffered in
+    // LDS (deeper register prefetch and a software-pipelined form that scored
+    // the next row tile under this one's exponentials both measured slower
+    // on the 32-layer workload: the waves then waited longer at the barrier).
+    auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
+    TileSR cur = to_sr(desc(0));
+    uint32_t nraw = desc(1);
+    stage_store(stage_load(cur), 0);
+    __syncthreads();
+    for (int tt = 0; tt < n_kt; ++tt) {
+        const int buf = tt & 1;
+        const bool more = tt + 1 < n_kt;
+        const TileSR nxt = to_sr(nraw);
+        nraw = desc(tt + 2);
+        decltype(stage_load(nxt)) st;
+        if (more)
+            st = stage_load(nxt);
+        if constexpr (R > 0) {
+            const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
+            if (need_mask)
+                tile_exact(cur, buf, std::true_type{});
+            else if (!tile_ref(buf))
+                tile_exact(cur, buf, std::false_type{});
+        }
+        if (more)
+            stage_store(st, buf ^ 1);
+        __syncthreads();
+        cur = nxt;
+    }
+
+    // The four lane groups of a row hold partial (max, sum) states: combine
+    // them; padded rows get +inf (every weight they would produce is 0).
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        float m = row_m[i], l = row_l[i];
+        merge_state(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16), c);
+        merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32), c);
+        const int local = (wave + i * kLseWaves) * kRowTile + li;   // packed row inside the item's block
+        if (lg == 0)
+            as_global(a.lse)[(size_t)blockIdx.x * a.lse_stride + local] =
+                (row_pos[i] < 0x3fffffff) ? m * c + __log2f(l) : INFINITY;
+    }
+}
+
+template <int D, bool KV8>
+__global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnArgs a)
+{
+    constexpr int NCH = D / 8;
+    constexpr int TILE = kKeyTile * 2 * D;
+    constexpr int NT = kLseWaves * 64;
+    using Stg = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];
+
+    const ItemDesc it = a.items[blockIdx.x];
+    if (it.n_rowtiles == 0 || it.n_ktiles == 0)
+        return;
+    const ProbDesc pr = a.probs[it.prob];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const Stg stg(threadIdx.x);
+    // this wave's row tiles: wave, wave + 8, ... below n_rowtiles
+    const int mine = wave < it.n_rowtiles ? (it.n_rowtiles - wave + kLseWaves - 1) / kLseWaves : 0;
+    switch (mine) {
+    case 0: lse_body<D, 0, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
+    case 1: lse_body<D, 1, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
+    case 2: lse_body<D, 2, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
+    case 3: lse_body<D, 3, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
+    default: lse_body<D, 4, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
+    }
+}
+
+// The items of a plan whose blocks hold at most kLseWaves *
+// kLseMaxRowTilesPerWave row tiles (the one-wave kernel's blocks: 4 * RT).
+hipError_t launch_attn_lse(int d, bool kv8, const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    if (n_items <= 0)
+        return hipSuccess;
+    const dim3 grid(n_items), block(kLseWaves * 64);
+    if (d == 128) {
+        if (kv8)
+            hipLaunchKernelGGL((attn_lse_kernel<128, true>), grid, block, 0, stream, args);
+        else
+            hipLaunchKernelGGL((attn_lse_kernel<128, false>), grid, block, 0, stream, args);
+    } else {
+        if (kv8)
+            hipLaunchKernelGGL((attn_lse_kernel<64, true>), grid, block, 0, stream, args);
+        else
+            hipLaunchKernelGGL((attn_lse_kernel<64, false>), grid, block, 0, stream, args);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace crkv

@@ -29,6 +29,7 @@ namespace crkv {
 hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_bf16_pair(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_q8(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_lse(int d, bool kv8, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_decode_bf16(int d, const DecodeArgs &args, int n_items, int n_pairs, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
@@ -403,7 +404,9 @@ struct Plan {
     std::vector<size_t> seg_base, tile_base, slot_base, partial_base;   // per problem
     size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0;
     size_t table_bytes = 0;     // plan tables (uploaded through the ring)
-    size_t scratch_bytes = 0;   // impact partials (workspace or library scratch)
+    size_t scratch_bytes = 0;   // impact partials, then the pass-1 rows (workspace or library scratch)
+    size_t lse_off = 0;         // byte offset of the pass-1 rows in the scratch
+    int lse_stride = 0;         // floats per item of the pass-1 rows (0: pass 1 inside pass 2's kernel)
     int max_keys = 0;
     int rt = 1;                 // row tiles per wave (wave kernel) or wave pair (pair kernel)
     int kernel = kBf16Wave;     // bf16 kernel of the launch
@@ -597,6 +600,49 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
     pl.off_slots = align_up(pl.off_tiles + pl.tiles.size() * sizeof(KTile), 256);
     pl.table_bytes = align_up(pl.off_slots + pl.slot_end.size() * sizeof(int32_t), 256);
     pl.scratch_bytes = std::max<size_t>(partial_floats * sizeof(float), 256);
+    // The one-wave kernel's pass 1 runs as its own kernel (attn_lse_kernel,
+    // two waves per SIMD) unless CRKV_SWEEP1=fused asks for the fused form.
+    const char *es = getenv("CRKV_SWEEP1");
+    if (bf16 && pl.kernel == kBf16Wave && !(es && strcmp(es, "fused") == 0)) {
+        pl.lse_stride = cap * kRowTile;
+        pl.lse_off = align_up(pl.scratch_bytes, 256);
+        pl.scratch_bytes = pl.lse_off + pl.items.size() * (size_t)pl.lse_stride * sizeof(float);
+    }
+}
+
+// Kernel arguments of a planned launch, tables at `dev`, scratch at `scratch`.
+AttnArgs make_args(const Plan &pl, int H, int H_kv, int d, const crkv_opts &o, const unsigned char *dev,
+                   void *scratch)
+{
+    AttnArgs args{};
+    args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
+    args.items = reinterpret_cast<const ItemDesc *>(dev + pl.off_items);
+    args.H = H;
+    args.H_kv = H_kv;
+    args.G = H / H_kv;
+    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
+    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    if (pl.lse_stride) {
+        args.lse_stride = pl.lse_stride;
+        args.lse = reinterpret_cast<float *>(static_cast<unsigned char *>(scratch) + pl.lse_off);
+    }
+    return args;
+}
+
+// The attention kernels of a launch: pass 1 on its own first when args.lse
+// is set, then the kernel the plan chose.
+hipError_t launch_attn_kernels(int dtype, int kernel, int rt, int d, const AttnArgs &args, int n_items,
+                               hipStream_t stream)
+{
+    hipError_t e = hipSuccess;
+    if (args.lse)
+        e = launch_attn_lse(d, dtype == CRKV_KV_Q8, args, n_items, stream);
+    if (e == hipSuccess)
+        e = dtype == CRKV_KV_Q8    ? launch_attn_q8(d, rt, args, n_items, stream)
+            : dtype != CRKV_BF16   ? launch_attn_f32(d, args, n_items, stream)
+            : kernel == kBf16Wave ? launch_attn_bf16_wave(d, rt, args, n_items, stream)
+                                   : launch_attn_bf16_pair(d, rt, args, n_items, stream);
+    return e;
 }
 
 // Writes the plan tables (with device addresses inside `dev`, the tables'
@@ -669,28 +715,18 @@ int check_topk_args(const float *impact, int n, int k, const int32_t *idx, int w
     return CRKV_OK;
 }
 
-// Enqueues the attention kernel the plan chose and the impact combine, with
-// the plan's tables at `dev` (device copy already enqueued on `stream`).
+// Enqueues the attention kernels the plan chose and the impact combine, with
+// the plan's tables at `dev` (device copy already enqueued on `stream`) and
+// its scratch at `scratch`.
 hipError_t launch_planned(const Plan &pl, int n_problems, int H, int H_kv, int d, const crkv_opts &o,
-                          const unsigned char *dev, hipStream_t stream)
+                          const unsigned char *dev, void *scratch, hipStream_t stream)
 {
-    AttnArgs args{};
-    args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
-    args.items = reinterpret_cast<const ItemDesc *>(dev + pl.off_items);
-    args.H = H;
-    args.H_kv = H_kv;
-    args.G = H / H_kv;
-    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
-    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-
+    const AttnArgs args = make_args(pl, H, H_kv, d, o, dev, scratch);
     hipError_t e = hipSuccess;
     if (o.timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
     if (e == hipSuccess)
-        e = o.dtype == CRKV_KV_Q8    ? launch_attn_q8(d, pl.rt, args, (int)pl.items.size(), stream)
-            : o.dtype != CRKV_BF16   ? launch_attn_f32(d, args, (int)pl.items.size(), stream)
-            : pl.kernel == kBf16Wave ? launch_attn_bf16_wave(d, pl.rt, args, (int)pl.items.size(), stream)
-                                     : launch_attn_bf16_pair(d, pl.rt, args, (int)pl.items.size(), stream);
+        e = launch_attn_kernels(o.dtype, pl.kernel, pl.rt, d, args, (int)pl.items.size(), stream);
     if (e == hipSuccess && o.timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
     if (e == hipSuccess)
@@ -1168,14 +1204,7 @@ int plan_create(const crkv_problem *problems, int n_problems, int H, int H_kv, i
     p->n_items = (int)pl.items.size();
     p->max_keys = pl.max_keys;
     p->topk = std::move(descs);
-    AttnArgs &args = p->args;
-    args.probs = reinterpret_cast<const ProbDesc *>(p->tables + pl.off_probs);
-    args.items = reinterpret_cast<const ItemDesc *>(p->tables + pl.off_items);
-    args.H = H;
-    args.H_kv = H_kv;
-    args.G = H / H_kv;
-    args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
-    args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    p->args = make_args(pl, H, H_kv, d, o, p->tables, p->scratch);
     *out = p.release();
     return CRKV_OK;
 }
@@ -1194,10 +1223,7 @@ int plan_launch(const crkv_plan *p, void *stream_ptr, void *const *timing_events
     if (timing_events && timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[0]), stream);
     if (e == hipSuccess)
-        e = p->dtype == CRKV_KV_Q8   ? launch_attn_q8(p->d, p->rt, p->args, p->n_items, stream)
-            : p->dtype != CRKV_BF16  ? launch_attn_f32(p->d, p->args, p->n_items, stream)
-            : p->kernel == kBf16Wave ? launch_attn_bf16_wave(p->d, p->rt, p->args, p->n_items, stream)
-                                     : launch_attn_bf16_pair(p->d, p->rt, p->args, p->n_items, stream);
+        e = launch_attn_kernels(p->dtype, p->kernel, p->rt, p->d, p->args, p->n_items, stream);
     if (e == hipSuccess && timing_events && timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[1]), stream);
     if (e == hipSuccess)
@@ -1512,7 +1538,7 @@ int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H
         scratch_release(sc, stream);
         return rc;
     }
-    const hipError_t e = launch_planned(pl, n_problems, H, H_kv, d, o, dev, stream);
+    const hipError_t e = launch_planned(pl, n_problems, H, H_kv, d, o, dev, sc.ptr, stream);
     plan_release(lease, stream);
     scratch_release(sc, stream);
     if (e != hipSuccess)
@@ -1551,7 +1577,7 @@ int crkv_attn_chunks_batched_static(const crkv_problem *problems, int n_problems
     hipError_t e = hipMemcpyAsync(base, host.data(), pl.table_bytes, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess)
         return hip_fail(e, "hipMemcpyAsync(static tables)");
-    e = launch_planned(pl, n_problems, H, H_kv, d, o, base, stream);
+    e = launch_planned(pl, n_problems, H, H_kv, d, o, base, base + partial_off, stream);
     if (e != hipSuccess)
         return hip_fail(e, "attention launch");
     return CRKV_OK;

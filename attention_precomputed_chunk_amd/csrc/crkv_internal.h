@@ -86,7 +86,14 @@ struct AttnArgs {
     int32_t H, H_kv, G;
     int32_t cross;          // 1: impact skips rows of the key's own segment
     float c_log2;           // log2(e) / sqrt(d)
+    int32_t lse_stride;     // floats of `lse` per work item (pass 1 run as its own kernel)
+    float *lse;             // [item][packed row of the item's block] log2-domain row lse, or null
 };
+
+// Pass 1 as its own kernel (attn_lse_kernel): kLseWaves waves per workgroup,
+// two per SIMD, the item's row tiles dealt to them round robin.
+constexpr int kLseWaves = 8;
+constexpr int kLseMaxRowTilesPerWave = 4;   // items of up to 32 row tiles
 
 // Decode step (q_len = 1): the keys of each (problem, KV head) are split into
 // ranges of key tiles; one workgroup per range writes a partial softmax state

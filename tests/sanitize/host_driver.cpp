@@ -30,6 +30,7 @@ struct ProbDesc;
 hipError_t launch_attn_bf16_wave(int, int, const AttnArgs &, int, hipStream_t) { launched("wave"); }
 hipError_t launch_attn_bf16_pair(int, int, const AttnArgs &, int, hipStream_t) { launched("pair"); }
 hipError_t launch_attn_q8(int, int, const AttnArgs &, int, hipStream_t) { launched("q8 attention"); }
+hipError_t launch_attn_lse(int, bool, const AttnArgs &, int, hipStream_t) { launched("pass 1"); }
 hipError_t launch_decode_bf16(int, const DecodeArgs &, int, int, hipStream_t) { launched("decode"); }
 hipError_t launch_attn_f32(int, const AttnArgs &, int, hipStream_t) { launched("f32"); }
 hipError_t launch_combine(const ProbDesc *, int, int, hipStream_t) { launched("combine"); }

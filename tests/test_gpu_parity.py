@@ -113,6 +113,24 @@ def test_forced_bf16_builds(case, build, monkeypatch):
     run_and_compare(wl, label="forced-%s%d-small%d" % (kernel, rt, case))
 
 
+@pytest.mark.parametrize("sweep1", ["split", "fused"])
+@pytest.mark.parametrize("rt", [4, 5, 7])
+@pytest.mark.parametrize("case", [2, 3, 4, 8])
+def test_wave_pass1_forms(case, rt, sweep1, monkeypatch):
+    """The one-wave kernel with pass 1 inside it (fused) or as its own
+    two-waves-per-SIMD kernel writing the row lse (split), against the
+    oracle on shapes whose rows span several workgroups."""
+    seed, doc, q, H, H_kv, d, dtype, mode = SMALL[case]
+    if mode == "cross" and rt > 5:
+        pytest.skip("no cross-document wave build with 7 row tiles")
+    monkeypatch.setenv("CRKV_BF16_KERNEL", "wave")
+    monkeypatch.setenv("CRKV_ROW_TILES", str(rt))
+    monkeypatch.setenv("CRKV_SWEEP1", sweep1)
+    say("pass 1", sweep1, "wave", rt, "small case", SMALL[case])
+    wl = workloads.custom(100 + seed, doc, q, H, H_kv, d, dtype=dtype, mode=mode, r=0.1, n_problems=2)
+    run_and_compare(wl, label="pass1-%s-wave%d-small%d" % (sweep1, rt, case))
+
+
 def rising_scores_workload(seed, mode):
     """Scores that climb by about 80 log2 units along the keys: channel 0 of
     every key grows with its position and channel 0 of every query row is
@@ -134,14 +152,16 @@ def rising_scores_workload(seed, mode):
     return wl
 
 
-@pytest.mark.parametrize("build", [None, ("wave", 4), ("wave", 7), ("pair", 6)],
-                         ids=["planner", "wave4", "wave7", "pair6"])
+@pytest.mark.parametrize("build", [None, ("wave", 4), ("wave", 7), ("pair", 6), ("wave", 7, "fused")],
+                         ids=["planner", "wave4", "wave7", "pair6", "wave7-fused"])
 def test_rising_scores(build, monkeypatch):
     """Sweep 1's exact-maximum path taken again and again (a row's maximum
     keeps rising), against the oracle."""
     if build:
         monkeypatch.setenv("CRKV_BF16_KERNEL", build[0])
         monkeypatch.setenv("CRKV_ROW_TILES", str(build[1]))
+        if len(build) > 2:
+            monkeypatch.setenv("CRKV_SWEEP1", build[2])
     say("rising scores", build)
     run_and_compare(rising_scores_workload(350, "query"), label="rising-%s" % (build,))
 
