@@ -74,11 +74,18 @@ class crkv_q8_seg(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("q8", ctypes.c_void_p), ("len", ctypes.c_int), ("kind", ctypes.c_int)]
 
 
+class crkv_plan_stat(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("row_tiles", ctypes.c_int), ("workgroups", ctypes.c_int),
+                ("pass1_separate", ctypes.c_int), ("split_blocks", ctypes.c_int), ("max_ranges", ctypes.c_int),
+                ("combine_workgroups", ctypes.c_int), ("pad", ctypes.c_int), ("model_cycles", ctypes.c_double),
+                ("work_cycles", ctypes.c_double), ("scratch_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 DECLARED = ["crkv_plan_create", "crkv_plan_launch", "crkv_plan_destroy", "crkv_q8_bytes", "crkv_quantize_q8", "crkv_opts_init", "crkv_attn_chunks", "crkv_topk", "crkv_attn_chunks_batched",
             "crkv_attn_chunks_batched_static", "crkv_static_scratch_bytes",
-            "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info",
+            "crkv_topk_batched", "crkv_budget", "crkv_workspace_size", "crkv_plan_info", "crkv_plan_stats",
             "crkv_decode_chunks_batched", "crkv_decode_workspace_size", "crkv_gather_kv",
             "crkv_scatter_kv", "crkv_rope_shift",
             "crkv_status_string", "crkv_last_error", "crkv_version"]
@@ -125,6 +132,9 @@ def lib():
                                      ctypes.POINTER(crkv_opts), ctypes.POINTER(c_int), ctypes.POINTER(c_int),
                                      ctypes.POINTER(c_int)]
         L.crkv_plan_info.restype = c_int
+        L.crkv_plan_stats.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
+                                      ctypes.POINTER(crkv_opts), ctypes.POINTER(crkv_plan_stat)]
+        L.crkv_plan_stats.restype = c_int
         L.crkv_decode_chunks_batched.argtypes = [ctypes.POINTER(crkv_problem), c_int, c_int, c_int, c_int,
                                                  ctypes.POINTER(crkv_opts)]
         L.crkv_decode_chunks_batched.restype = c_int
@@ -365,6 +375,22 @@ def crkv_plan_info(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: st
     _check(lib().crkv_plan_info(arr, len(keep), H, H_kv, d, ctypes.byref(o), ctypes.byref(k),
                                 ctypes.byref(rt), ctypes.byref(wg)))
     return {"kernel": PLAN_KERNELS[k.value], "row_tiles": rt.value, "workgroups": wg.value}
+
+
+def crkv_plan_stats(problems: Sequence[dict], H: int, H_kv: int, d: int, mode: str = "query",
+                    dtype: Optional[int] = None) -> dict:
+    """The planner's plan in detail: kernel, row tiles, workgroups, whether
+    pass 1 runs on its own, blocks split into key ranges (and the most ranges
+    of one block), combine workgroups, the modelled duration and work (shader
+    cycles; imbalance = duration * 256 / work - 1), and the scratch size."""
+    keep, arr = _problems(problems)
+    o = make_opts(_batch_dtype(problems) if dtype is None else dtype, mode, stream=0)
+    st = crkv_plan_stat()
+    _check(lib().crkv_plan_stats(arr, len(keep), H, H_kv, d, ctypes.byref(o), ctypes.byref(st)))
+    out = {f: getattr(st, f) for f, _ in crkv_plan_stat._fields_ if f != "pad"}
+    out["kernel"] = PLAN_KERNELS[st.kernel]
+    out["imbalance"] = st.model_cycles * 256 / st.work_cycles - 1 if st.work_cycles else 0.0
+    return out
 
 
 def crkv_topk(impact, n: int, k: int, idx, stream=None):

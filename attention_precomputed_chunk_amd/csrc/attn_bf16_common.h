@@ -305,6 +305,21 @@ __device__ __forceinline__ void mask_scores(Spair &s, int lim, int lg)
     }
 }
 
+// Log2-domain lse of packed row `local` of an item's row block, from the
+// pass-1 states of the block's ranges merged in range order (the same value
+// in every range's item of the block).
+__device__ __forceinline__ float merged_lse(const AttnArgs &a, const ItemDesc &it, int local, float c)
+{
+    const gptr<const f32x2> st = as_global(reinterpret_cast<const f32x2 *>(a.state)) + (size_t)it.state + local;
+    const f32x2 s0 = st[0];
+    float m = s0.x, l = s0.y;
+    for (int r = 1; r < it.n_ranges; ++r) {
+        const f32x2 s = st[(size_t)r * a.cap_rows];
+        merge_state(m, l, s.x, s.y, c);
+    }
+    return m * c + __log2f(l);
+}
+
 // Q^T fragments of row tile t: packed row r = 16 t + li is query row r / G of
 // head kv_head * G + r % G; rows past the packed total are padding (zero Q,
 // position beyond every key).

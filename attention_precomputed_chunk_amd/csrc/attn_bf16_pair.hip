@@ -45,7 +45,7 @@
 namespace crkv {
 
 
-template <int D, int RT, bool CROSS>
+template <int D, int RT, bool CROSS, bool LSE_IN>
 __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnArgs a)
 {
     constexpr int RT1 = RT / 2;                // row tiles per wave in sweep 1
@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     __shared__ __attribute__((aligned(16))) unsigned char lds_v[3][TILE];
     __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][kWaves][RT][64];
     __shared__ __attribute__((aligned(16))) float lds_imp[2][kWaves][kKeyTile];
-    __shared__ float lds_lse[kWaves * RT * kRowTile];
+    __shared__ float lds_lse[LSE_IN ? 1 : kWaves * RT * kRowTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,7 +72,8 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     const ProbDesc pr = a.probs[it.prob];
     const int G = a.G;
     const float c = a.c_log2;
-    const int n_kt = it.n_ktiles;
+    const int n_kt = it.n_ktiles;   // key tiles kt0 .. kt0 + n_kt - 1 of the problem's list
+    const int kt0 = it.kt_begin;
     if (n_kt == 0)
         return;
 
@@ -85,11 +86,12 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
         const int d = 16 * dt + 4 * (li & 3);
         return key * ROW + (((d >> 3) ^ vswz<NCH>(key)) << 4) + (d & 7) * 2;
     };
-    auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
+    auto desc = [&](int tt) { return load_tile(pr.tiles, kt0 + min(tt, n_kt - 1), lane); };
     auto min_pos = [&](int t0) { return pr.pos0 + (t0 * kRowTile) / G; };
 
     // ---------------------------------------------------------------- sweep 1: row lse (all waves)
-    {
+    // (with LSE_IN pass 1 ran as attn_lse_kernel: one state per key range)
+    if constexpr (!LSE_IN) {
         const int t0 = it.tile_begin + wave * RT1;
         const int wave_min_pos = min_pos(t0);
         bf16x8 qf[RT1][KS];
@@ -203,7 +205,11 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             load_q_rows<KS>(pr, it, G, t0 + rt, li, lg, qf[rt], row_pos[rt]);
-            lse2[rt] = lds_lse[(pair * RT + rt) * kRowTile + li];
+            if constexpr (LSE_IN)
+                lse2[rt] = (row_pos[rt] < 0x3fffffff) ? merged_lse(a, it, (pair * RT + rt) * kRowTile + li, c)
+                                                      : INFINITY;
+            else
+                lse2[rt] = lds_lse[(pair * RT + rt) * kRowTile + li];
         }
         auto tile = [&](TileSR kt, int buf, auto mask_tag) {
             constexpr bool MASK = decltype(mask_tag)::value;
@@ -323,7 +329,23 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
         }
 
         // ------------------------------------------------------------ epilogue: out rows
+        // (a block split into key ranges writes this range's fp32 partial
+        // rows; attn_out_combine_kernel sums them)
         const int packed_total = G * pr.rows;
+        if (LSE_IN && it.n_ranges > 1) {
+            const gptr<f32x4> part = as_global(reinterpret_cast<f32x4 *>(a.opart + it.opart)) +
+                                     (size_t)it.range * (a.cap_rows * D / 4);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int local = (pair * RT + rt) * kRowTile + li;
+                if ((t0 + rt) * kRowTile + li >= packed_total)
+                    continue;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    part[(size_t)local * (D / 4) + 4 * dt + lg] = o[rt][dt];
+            }
+            return;
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int r = (t0 + rt) * kRowTile + li;
@@ -347,13 +369,25 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     }
 }
 
+// args.state non-null: pass 1 already ran (attn_lse_kernel) and sweep 1 is skipped.
+template <int D, int RT, bool LSE_IN>
+static void launch_pair_rt2(const AttnArgs &args, int n_items, hipStream_t stream)
+{
+    if (args.cross)
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, RT, true, LSE_IN>), dim3(n_items), dim3(kWsThreads), 0, stream,
+                           args);
+    else
+        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, RT, false, LSE_IN>), dim3(n_items), dim3(kWsThreads), 0, stream,
+                           args);
+}
+
 template <int D, int RT>
 static void launch_pair_rt(const AttnArgs &args, int n_items, hipStream_t stream)
 {
-    if (args.cross)
-        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, RT, true>), dim3(n_items), dim3(kWsThreads), 0, stream, args);
+    if (args.state)
+        launch_pair_rt2<D, RT, true>(args, n_items, stream);
     else
-        hipLaunchKernelGGL((attn_bf16_pair_kernel<D, RT, false>), dim3(n_items), dim3(kWsThreads), 0, stream, args);
+        launch_pair_rt2<D, RT, false>(args, n_items, stream);
 }
 
 template <int D>

@@ -115,7 +115,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         return key * ROW + (((d >> 3) ^ vswz<NCH>(key)) << 4) + (d & 7) * 2;
     };
 
-    const int n_kt = it.n_ktiles;
+    const int n_kt = it.n_ktiles;   // key tiles kt0 .. kt0 + n_kt - 1 of the problem's list
+    const int kt0 = it.kt_begin;
     // ---------------------------------------------------------------- sweep 1: row lse
     float row_m[RT], row_l[RT];
 #pragma unroll
@@ -215,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
 
     // Descriptors are loaded two tiles ahead of use and data one tile ahead;
     // a descriptor reaches scalar registers one iteration after its load.
-    auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
+    auto desc = [&](int tt) { return load_tile(pr.tiles, kt0 + min(tt, n_kt - 1), lane); };
     if (!LSE_IN && n_kt > 0) {
         TileSR cur = to_sr(desc(0));
         uint32_t nraw = desc(1);
@@ -242,16 +243,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     }
 
     // Combine the four lane groups of each row into its log2-domain lse;
-    // padded rows get +inf so every weight they would produce is 0.
-    // (or read them: with LSE_IN, pass 1 ran as attn_lse_kernel on the same items)
+    // padded rows get +inf so every weight they would produce is 0. With
+    // LSE_IN pass 1 ran as attn_lse_kernel, one state per range of the block
+    // (written for the block's real row tiles only).
     float lse2[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         if constexpr (LSE_IN) {
-            // pass 1 writes the item's real row tiles only; padded rows get +inf here
-            lse2[rt] = (row_pos[rt] < 0x3fffffff)
-                           ? as_global(a.lse)[(size_t)blockIdx.x * a.lse_stride + (wave * RT + rt) * kRowTile + li]
-                           : INFINITY;
+            lse2[rt] = (row_pos[rt] < 0x3fffffff) ? merged_lse(a, it, (wave * RT + rt) * kRowTile + li, c) : INFINITY;
         } else {
             float m = row_m[rt], l = row_l[rt];
             merge_state(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16), c);
@@ -490,6 +489,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     }
 
     // ---------------------------------------------------------------- epilogue: out rows
+    // (a block split into key ranges writes this range's fp32 partial rows;
+    // attn_out_combine_kernel sums them)
+    if (LSE_IN && it.n_ranges > 1) {
+        const gptr<f32x4> part = as_global(reinterpret_cast<f32x4 *>(a.opart + it.opart)) +
+                                 (size_t)it.range * (a.cap_rows * D / 4);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int local = (wave * RT + rt) * kRowTile + li;
+            if ((t0 + rt) * kRowTile + li >= packed_total)
+                continue;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                part[(size_t)local * (D / 4) + 4 * dt + lg] = o[rt][dt];
+        }
+        return;
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int r = (t0 + rt) * kRowTile + li;
@@ -525,11 +540,11 @@ static void launch_wave_rt2(const AttnArgs &args, int n_items, hipStream_t strea
                        args);
 }
 
-// args.lse non-null: pass 1 already ran (attn_lse_kernel) and pass 2 reads it.
+// args.state non-null: pass 1 already ran (attn_lse_kernel) and pass 2 reads it.
 template <int D, int RT, bool KV8>
 static void launch_wave_rt(const AttnArgs &args, int n_items, hipStream_t stream)
 {
-    if (args.lse)
+    if (args.state)
         launch_wave_rt2<D, RT, KV8, true>(args, n_items, stream);
     else
         launch_wave_rt2<D, RT, KV8, false>(args, n_items, stream);
@@ -542,19 +557,23 @@ hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_item
     if (args.cross && rt > kWaveMaxRowTilesCross)
         return hipErrorInvalidValue;   // no such build; the planner never asks for it
     if (d == 128) {
-        if (rt == 7)
-            launch_wave_rt<128, 7, false>(args, n_items, stream);
-        else if (rt == 5)
-            launch_wave_rt<128, 5, false>(args, n_items, stream);
-        else
-            launch_wave_rt<128, 4, false>(args, n_items, stream);
+        switch (rt) {
+        case 1: launch_wave_rt<128, 1, false>(args, n_items, stream); break;
+        case 2: launch_wave_rt<128, 2, false>(args, n_items, stream); break;
+        case 4: launch_wave_rt<128, 4, false>(args, n_items, stream); break;
+        case 5: launch_wave_rt<128, 5, false>(args, n_items, stream); break;
+        case 7: launch_wave_rt<128, 7, false>(args, n_items, stream); break;
+        default: return hipErrorInvalidValue;   // no such build; the planner never asks for it
+        }
     } else {
-        if (rt == 7)
-            launch_wave_rt<64, 7, false>(args, n_items, stream);
-        else if (rt == 5)
-            launch_wave_rt<64, 5, false>(args, n_items, stream);
-        else
-            launch_wave_rt<64, 4, false>(args, n_items, stream);
+        switch (rt) {
+        case 1: launch_wave_rt<64, 1, false>(args, n_items, stream); break;
+        case 2: launch_wave_rt<64, 2, false>(args, n_items, stream); break;
+        case 4: launch_wave_rt<64, 4, false>(args, n_items, stream); break;
+        case 5: launch_wave_rt<64, 5, false>(args, n_items, stream); break;
+        case 7: launch_wave_rt<64, 7, false>(args, n_items, stream); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }

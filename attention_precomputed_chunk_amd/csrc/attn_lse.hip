@@ -1,9 +1,13 @@
 // Pass 1 of the attention (the row log-sum-exp) as a kernel of its own, for
-// gfx950 (CDNA4), run before the one-wave kernel's pass 2 on the same work
-// items (TurboRAG summary, the causal attention equation; CacheBlend
-// summary, the selective-recompute listing's softmax over every key):
+// gfx950 (CDNA4), run before pass 2 on the same work items (TurboRAG summary,
+// the causal attention equation; CacheBlend summary, the selective-recompute
+// listing's softmax over every key):
 //   lse_j = log sum_i exp(q_j . k_i / sqrt(d))   over the keys visible to row j
-// stored in the log2 domain (lse_j / ln 2) per packed row of each item.
+// Each work item covers one range of its row block's key tiles and stores,
+// per packed row, the partial state of that range: the largest raw score m
+// and l = sum_i exp2((s_ji - m) c) with c = log2(e) / sqrt(d). Pass 2 merges
+// the states of its block's ranges in range order, so every range of a block
+// uses the same lse, and lse_j / ln 2 = m c + log2 l.
 //
 // Why a separate kernel: a wave issues its vector and matrix instructions in
 // order, and in the one-wave-per-SIMD kernel the two barely overlap; a second
@@ -39,6 +43,7 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
     const int G = a.G;
     const float c = a.c_log2;
     const int n_kt = it.n_ktiles;
+    const int kt0 = it.kt_begin;
 
     int row_pos[RR];
     bf16x8 qf[RR][KS];
@@ -153,7 +158,7 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
     // LDS (deeper register prefetch and a software-pipelined form that scored
     // the next row tile under this one's exponentials both measured slower
     // on the 32-layer workload: the waves then waited longer at the barrier).
-    auto desc = [&](int tt) { return load_tile(pr.tiles, min(tt, n_kt - 1), lane); };
+    auto desc = [&](int tt) { return load_tile(pr.tiles, kt0 + min(tt, n_kt - 1), lane); };
     TileSR cur = to_sr(desc(0));
     uint32_t nraw = desc(1);
     stage_store(stage_load(cur), 0);
@@ -180,7 +185,9 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
     }
 
     // The four lane groups of a row hold partial (max, sum) states: combine
-    // them; padded rows get +inf (every weight they would produce is 0).
+    // them into the range's state (rows that see no key of the range keep
+    // (-inf, 0); padded rows are never read).
+    const gptr<f32x2> state = as_global(reinterpret_cast<f32x2 *>(a.state)) + (size_t)it.state + (size_t)it.range * a.cap_rows;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         float m = row_m[i], l = row_l[i];
@@ -188,8 +195,7 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
         merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32), c);
         const int local = (wave + i * kLseWaves) * kRowTile + li;   // packed row inside the item's block
         if (lg == 0)
-            as_global(a.lse)[(size_t)blockIdx.x * a.lse_stride + local] =
-                (row_pos[i] < 0x3fffffff) ? m * c + __log2f(l) : INFINITY;
+            state[local] = f32x2{m, l};
     }
 }
 
@@ -222,7 +228,7 @@ __global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnA
 }
 
 // The items of a plan whose blocks hold at most kLseWaves *
-// kLseMaxRowTilesPerWave row tiles (the one-wave kernel's blocks: 4 * RT).
+// kLseMaxRowTilesPerWave row tiles (the bf16 kernels' blocks: 4 * RT).
 hipError_t launch_attn_lse(int d, bool kv8, const AttnArgs &args, int n_items, hipStream_t stream)
 {
     if (n_items <= 0)
@@ -239,6 +245,57 @@ hipError_t launch_attn_lse(int d, bool kv8, const AttnArgs &args, int n_items, h
         else
             hipLaunchKernelGGL((attn_lse_kernel<64, false>), grid, block, 0, stream, args);
     }
+    return hipGetLastError();
+}
+
+// Output rows of split row blocks: each range's pass 2 wrote its fp32
+// partial sum_i p_ji v_i over the range's keys (p already normalised by the
+// block's full lse), so out_j is their sum, taken in range order (the same
+// result on every run), rounded once to bf16. One workgroup per (split
+// block, 16-row tile); a thread sums 4 columns of a row.
+template <int D>
+__global__ void __launch_bounds__(256) attn_out_combine_kernel(const CombineArgs a)
+{
+    constexpr int V4 = D / 4;   // float4 per row
+    const OutCombItem ci = a.items[blockIdx.x];
+    const ProbDesc pr = a.probs[ci.prob];
+    const int G = a.G;
+    const int packed_total = G * pr.rows;
+    const gptr<const f32x4> src = as_global(reinterpret_cast<const f32x4 *>(a.opart + ci.opart));
+    const size_t stride4 = (size_t)a.range_stride / 4;
+#pragma unroll
+    for (int e0 = 0; e0 < kRowTile * V4; e0 += 256) {
+        const int e = e0 + threadIdx.x;
+        const int lr = e / V4, c4 = e - (e / V4) * V4;
+        const int r = ci.tile * kRowTile + lr;
+        if (e >= kRowTile * V4 || r >= packed_total)
+            continue;
+        f32x4 acc = src[(size_t)lr * V4 + c4];
+        for (int k = 1; k < ci.n_ranges; ++k) {
+            const f32x4 v = src[k * stride4 + (size_t)lr * V4 + c4];
+            acc[0] += v[0];
+            acc[1] += v[1];
+            acc[2] += v[2];
+            acc[3] += v[3];
+        }
+        const int j = r / G;
+        const int h = ci.kv_head * G + (r - j * G);
+        const __bf16 b0 = (__bf16)acc[0], b1 = (__bf16)acc[1], b2 = (__bf16)acc[2], b3 = (__bf16)acc[3];
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        const gptr<uint16_t> orow = as_global(reinterpret_cast<uint16_t *>(pr.out)) + ((size_t)h * pr.rows + j) * D;
+        *reinterpret_cast<gptr<u32x2>>(orow + 4 * c4) = u32x2{lo, hi};
+    }
+}
+
+hipError_t launch_attn_out_combine(int d, const CombineArgs &args, int n_items, hipStream_t stream)
+{
+    if (n_items <= 0)
+        return hipSuccess;
+    if (d == 128)
+        hipLaunchKernelGGL((attn_out_combine_kernel<128>), dim3(n_items), dim3(256), 0, stream, args);
+    else
+        hipLaunchKernelGGL((attn_out_combine_kernel<64>), dim3(n_items), dim3(256), 0, stream, args);
     return hipGetLastError();
 }
 

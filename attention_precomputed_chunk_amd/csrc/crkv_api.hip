@@ -30,6 +30,7 @@ hipError_t launch_attn_bf16_wave(int d, int rt, const AttnArgs &args, int n_item
 hipError_t launch_attn_bf16_pair(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_q8(int d, int rt, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_attn_lse(int d, bool kv8, const AttnArgs &args, int n_items, hipStream_t stream);
+hipError_t launch_attn_out_combine(int d, const CombineArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_decode_bf16(int d, const DecodeArgs &args, int n_items, int n_pairs, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs &args, int n_items, hipStream_t stream);
 hipError_t launch_combine(const ProbDesc *probs, int n_probs, int max_keys, hipStream_t stream);
@@ -401,15 +402,21 @@ struct Plan {
     std::vector<KTile> tiles;
     std::vector<int32_t> slot_end;
     std::vector<ItemDesc> items;
+    std::vector<OutCombItem> comb;   // row tiles of blocks split into key ranges
     std::vector<size_t> seg_base, tile_base, slot_base, partial_base;   // per problem
-    size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0;
+    size_t off_probs = 0, off_items = 0, off_segs = 0, off_tiles = 0, off_slots = 0, off_comb = 0;
     size_t table_bytes = 0;     // plan tables (uploaded through the ring)
-    size_t scratch_bytes = 0;   // impact partials, then the pass-1 rows (workspace or library scratch)
-    size_t lse_off = 0;         // byte offset of the pass-1 rows in the scratch
-    int lse_stride = 0;         // floats per item of the pass-1 rows (0: pass 1 inside pass 2's kernel)
+    size_t scratch_bytes = 0;   // impact partials, pass-1 states, output partials (workspace or library scratch)
+    size_t state_off = 0;       // byte offset of the pass-1 states in the scratch
+    size_t opart_off = 0;       // byte offset of the output partials in the scratch
+    bool lse_kernel = false;    // pass 1 runs as attn_lse_kernel (else inside pass 2's kernel)
+    int cap_rows = 0;           // packed rows per block
     int max_keys = 0;
     int rt = 1;                 // row tiles per wave (wave kernel) or wave pair (pair kernel)
     int kernel = kBf16Wave;     // bf16 kernel of the launch
+    int64_t model_cycles = 0;   // modelled duration of pass 2's kernel (the planner's cost model)
+    int64_t work_cycles = 0;    // modelled work of its items, summed
+    int split_blocks = 0, max_ranges = 1;
 };
 
 int64_t packed_rows(const crkv_problem &p, int G, int mode)
@@ -418,6 +425,12 @@ int64_t packed_rows(const crkv_problem &p, int G, int mode)
     for (int c = 0; c <= p.m; ++c)
         n += p.chunk_len[c];
     return (int64_t)G * (mode == CRKV_IMPACT_QUERY_ROWS ? p.q_len : n);
+}
+
+int64_t step_cycles(int kernel, int rt)
+{
+    return kernel == kBf16Wave ? kWaveStepFixed + (int64_t)kWaveStepPerTile * rt
+                               : kPairStepFixed + (int64_t)kPairStepPerTile * rt;
 }
 
 // The bf16 kernel and its row tiles per wave (or wave pair) for a launch.
@@ -439,9 +452,8 @@ void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, 
         if (ek && strcmp(ek, k == kBf16Wave ? "wave" : "pair") != 0)
             continue;
         const int *choices = k == kBf16Wave ? kWaveRowTiles : kPairRowTiles;
-        const int64_t fixed = k == kBf16Wave ? kWaveStepFixed : kPairStepFixed;
-        const int64_t per = k == kBf16Wave ? kWaveStepPerTile : kPairStepPerTile;
-        for (int c = 0; c < 3; ++c) {
+        const int n_choices = k == kBf16Wave ? kNumWaveRowTiles : 3;
+        for (int c = 0; c < n_choices; ++c) {
             const int r = choices[c];
             if (forced_rt && r != forced_rt)
                 continue;
@@ -464,7 +476,7 @@ void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, 
                     steps += (pos0 + last_row / G + kKeyTile) / kKeyTile;
                 }
             }
-            const int64_t cost = steps * (fixed + per * r);
+            const int64_t cost = steps * step_cycles(k, r);
             if (cost <= best_cost) {   // ties go to the later (larger) build
                 best_cost = cost;
                 kernel = k;
@@ -474,12 +486,223 @@ void choose_bf16(const crkv_problem *problems, int n_problems, int G, int mode, 
     }
 }
 
-// Builds the plan for a validated batch. Work items are ordered so that the
-// row blocks of one (problem, KV head) land on the same XCD (workgroup i runs
-// on XCD i % 8) next to each other in dispatch order, and so share their K/V
-// reads through that XCD's L2; groups are dealt to XCDs longest first.
+// A row block before it is cut into key ranges: its item fields except the
+// range ones, and every key tile its last row sees.
+struct Block {
+    ItemDesc it;
+    int n_kt;
+    int n_ranges = 1;
+};
+using Groups = std::vector<std::vector<Block>>;   // per (problem, KV head)
+
+constexpr int kXcd = 8;                 // workgroup i runs on XCD i % 8
+constexpr int kCUsPerXcd = kCUs / kXcd;
+constexpr int64_t kItemOverheadSteps = 2;   // Q load, lse, epilogue of a workgroup, in key steps
+constexpr int64_t kLaunchCycles = 8000;     // one more kernel in the stream (about 3.5 us)
+constexpr int64_t kBytesPerCycle = 1800;    // HBM bytes per shader cycle, streaming (about 4 TB/s)
+
+// Key tiles of range r of a block cut into n ranges of nearly equal length.
+inline int range_begin(int n_kt, int n, int r) { return (int)((int64_t)r * n_kt / n); }
+
+// Dispatch order: groups longest first, each to the XCD with the least
+// modelled work so far, so that the row blocks (and key ranges) of one
+// (problem, KV head) run on the same XCD and share their K/V reads through
+// its L2; on each XCD the longest items first, so that its last items, which
+// set when it finishes, are short (a group's items have nearly equal key
+// counts and stay next to each other). The model: on each XCD the items start
+// in that order on whichever of its CUs frees first (one workgroup per CU),
+// each taking (key tiles + fixed part) steps of `step` cycles.
+struct Dealer {
+    std::vector<std::pair<int64_t, int>> order;   // (cost, group)
+    std::vector<int> xcd;                         // per group
+    std::vector<int32_t> n_kt[kXcd];              // per XCD: key tiles of its items
+    std::vector<int64_t> cu;
+
+    void assign(const Groups &groups, int64_t step)
+    {
+        order.clear();
+        for (size_t g = 0; g < groups.size(); ++g) {
+            int64_t c = 0;
+            for (const Block &b : groups[g])
+                c += (b.n_kt + kItemOverheadSteps * b.n_ranges) * step;
+            order.emplace_back(c, (int)g);
+        }
+        std::stable_sort(order.begin(), order.end(),
+                         [](const std::pair<int64_t, int> &x, const std::pair<int64_t, int> &y) {
+                             return x.first > y.first;
+                         });
+        xcd.assign(groups.size(), 0);
+        int64_t load[kXcd] = {};
+        for (const auto &o : order) {
+            const int x = (int)(std::min_element(load, load + kXcd) - load);
+            xcd[o.second] = x;
+            load[x] += o.first;
+        }
+    }
+
+    // Modelled duration of the items.
+    int64_t model(const Groups &groups, int64_t step)
+    {
+        assign(groups, step);
+        for (auto &v : n_kt)
+            v.clear();
+        for (const auto &o : order)
+            for (const Block &b : groups[o.second])
+                for (int r = 0; r < b.n_ranges; ++r)
+                    n_kt[xcd[o.second]].push_back(range_begin(b.n_kt, b.n_ranges, r + 1) -
+                                                  range_begin(b.n_kt, b.n_ranges, r));
+        int64_t makespan = 0;
+        for (auto &v : n_kt) {
+            std::sort(v.begin(), v.end(), std::greater<int32_t>());
+            cu.assign(kCUsPerXcd, 0);   // min-heap of the CUs' free times
+            for (int32_t n : v) {
+                std::pop_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+                cu.back() += (n + kItemOverheadSteps) * step;
+                makespan = std::max(makespan, cu.back());
+                std::push_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+            }
+        }
+        return makespan;
+    }
+
+    // The work items in dispatch order (workgroup i runs on XCD i % 8).
+    void emit(const Groups &groups, int64_t step, std::vector<ItemDesc> &out)
+    {
+        assign(groups, step);
+        std::vector<std::vector<ItemDesc>> q(kXcd);
+        for (const auto &o : order)
+            for (const Block &b : groups[o.second])
+                for (int r = 0; r < b.n_ranges; ++r) {
+                    ItemDesc it = b.it;
+                    it.kt_begin = range_begin(b.n_kt, b.n_ranges, r);
+                    it.n_ktiles = range_begin(b.n_kt, b.n_ranges, r + 1) - it.kt_begin;
+                    it.range = r;
+                    it.n_ranges = b.n_ranges;
+                    q[xcd[o.second]].push_back(it);
+                }
+        size_t depth = 0;
+        for (auto &v : q) {
+            std::stable_sort(v.begin(), v.end(),
+                             [](const ItemDesc &x, const ItemDesc &y) { return x.n_ktiles > y.n_ktiles; });
+            depth = std::max(depth, v.size());
+        }
+        ItemDesc empty{};   // n_rowtiles = 0: the workgroup exits at once
+        for (size_t d = 0; d < depth; ++d)
+            for (int x = 0; x < kXcd; ++x)
+                out.push_back(d < q[x].size() ? q[x][d] : empty);
+        while (!out.empty() && out.back().n_rowtiles == 0)
+            out.pop_back();
+    }
+};
+
+// Cuts row blocks into key ranges where the modelled duration drops. A block
+// of one (problem, KV head) otherwise streams all of its keys in one
+// workgroup: a batch with few row blocks (one problem, short query) leaves
+// most of the chip idle, and one with blocks of very different lengths
+// (ragged requests) finishes on its longest ones. Candidates aim every item
+// at 1/4 .. 4 times the per-CU share of the work; a block gets ceil(cost /
+// aim) ranges of at least kMinRangeTiles key tiles, and the candidate with
+// the least modelled duration wins (no split on ties). A split costs
+// the fp32 output partials (written, then read by the combine), and one more
+// kernel (the combine, plus pass 1 on its own for plans that would fuse it).
+// CRKV_KEY_SPLIT = off, or a number of ranges for every block (tests).
+void choose_ranges(Groups &groups, int64_t step, int cap_rows, int d, bool lse_kernel_anyway)
+{
+    const char *e = getenv("CRKV_KEY_SPLIT");
+    if (e && strcmp(e, "off") == 0)
+        return;
+    if (e && atoi(e) > 0) {
+        const int n = atoi(e);
+        for (auto &g : groups)
+            for (Block &b : g)
+                b.n_ranges = std::max(1, std::min(n, b.n_kt));
+        return;
+    }
+    // The choice depends only on the blocks' key tiles and row tiles, the
+    // step cost, d and the pass-1 form: batches of one shape (every call of
+    // a serving loop) reuse it.
+    std::vector<int64_t> sig;
+    sig.reserve(4 + 2 * groups.size() * (groups.empty() ? 0 : groups[0].size()));
+    sig.push_back(step);
+    sig.push_back(d);
+    sig.push_back(lse_kernel_anyway);
+    sig.push_back((int64_t)groups.size());
+    for (auto &g : groups) {
+        sig.push_back(-(int64_t)g.size());
+        for (const Block &b : g)
+            sig.push_back(((int64_t)b.n_kt << 20) | b.it.n_rowtiles);
+    }
+    static std::mutex memo_mu;
+    static std::map<std::vector<int64_t>, std::vector<int>> memo;
+    {
+        std::lock_guard<std::mutex> lk(memo_mu);
+        auto it = memo.find(sig);
+        if (it != memo.end()) {
+            size_t i = 0;
+            for (auto &g : groups)
+                for (Block &b : g)
+                    b.n_ranges = it->second.empty() ? 1 : it->second[i++];
+            return;
+        }
+    }
+    auto remember = [&](const std::vector<int> &r) {
+        std::lock_guard<std::mutex> lk(memo_mu);
+        if (memo.size() >= 64)
+            memo.clear();
+        memo.emplace(std::move(sig), r);
+    };
+    static thread_local Dealer dealer;
+    int64_t work = 0;
+    for (auto &g : groups)
+        for (const Block &b : g)
+            work += (b.n_kt + kItemOverheadSteps) * step;
+    int64_t best = dealer.model(groups, step);
+    if (best * kCUs <= work + work / 32) {
+        remember({});
+        return;   // within 3 % of an even spread already: nothing for ranges to gain
+    }
+    std::vector<int> best_r;   // empty: no split
+    int64_t last_aim = -1;
+    for (int g8 : {2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32}) {   // aim = g8 / 8 of the per-CU share
+        const int64_t aim = std::max<int64_t>(work * g8 / ((int64_t)kCUs * 8), (kMinRangeTiles + kItemOverheadSteps) * step);
+        if (aim == last_aim)
+            continue;
+        last_aim = aim;
+        int64_t opart_bytes = 0, cand_work = 0, cand_max = 0;
+        std::vector<int> r;
+        for (auto &g : groups)
+            for (Block &b : g) {
+                const int64_t cost = (b.n_kt + kItemOverheadSteps) * step;
+                const int64_t want = (cost + aim - 1) / aim;
+                b.n_ranges = (int)std::max<int64_t>(1, std::min<int64_t>(want, b.n_kt / kMinRangeTiles));
+                if (b.n_ranges > 1)
+                    opart_bytes += (int64_t)b.n_ranges * b.it.n_rowtiles * kRowTile * d * 4;
+                cand_work += (b.n_kt + kItemOverheadSteps * b.n_ranges) * step;
+                cand_max = std::max(cand_max, ((b.n_kt + b.n_ranges - 1) / b.n_ranges + kItemOverheadSteps) * step);
+                r.push_back(b.n_ranges);
+            }
+        if (opart_bytes == 0 || opart_bytes > ((int64_t)1 << 32))   // offsets are int32 floats
+            continue;
+        const int64_t extra = 2 * opart_bytes / kBytesPerCycle + kLaunchCycles + (lse_kernel_anyway ? 0 : kLaunchCycles);
+        if (std::max(cand_work / kCUs, cand_max) + extra >= best)
+            continue;   // cannot win
+        const int64_t t = dealer.model(groups, step) + extra;
+        if (t < best) {
+            best = t;
+            best_r = std::move(r);
+        }
+    }
+    size_t i = 0;
+    for (auto &g : groups)
+        for (Block &b : g)
+            b.n_ranges = best_r.empty() ? 1 : best_r[i++];
+    remember(best_r);
+}
+
+// Builds the plan for a validated batch (key_ranges = false: no block is cut
+// into key ranges, whatever the model says).
 void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
-                const crkv_opts &o)
+                const crkv_opts &o, bool key_ranges = true)
 {
     const int G = H / H_kv;
     const bool q8 = o.dtype == CRKV_KV_Q8;
@@ -489,13 +712,21 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
     else
         pl.rt = 1;
     const int cap = bf16 ? kWaves * pl.rt : 1;   // row tiles per workgroup
-    struct Group {
-        int64_t cost;
-        std::vector<ItemDesc> items;
-    };
-    std::vector<Group> groups;
+    pl.cap_rows = cap * kRowTile;
+    Groups groups;
     size_t partial_floats = 0;
     pl.probs.resize(n_problems);
+    {
+        size_t n_tiles = 0, n_segs = 0;
+        for (int pi = 0; pi < n_problems; ++pi) {
+            n_segs += problems[pi].m + 1;
+            for (int c = 0; c <= problems[pi].m; ++c)
+                n_tiles += (problems[pi].chunk_len[c] + kKeyTile - 1) / kKeyTile;
+        }
+        pl.tiles.reserve(n_tiles);
+        pl.segs.reserve(n_segs);
+        groups.reserve((size_t)n_problems * H_kv);
+    }
     for (int pi = 0; pi < n_problems; ++pi) {
         const crkv_problem &p = problems[pi];
         int32_t n_doc = 0;
@@ -545,76 +776,113 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
         pd.n_slots = n_slots;
         pl.max_keys = std::max(pl.max_keys, (int)N);
         for (int kv = 0; kv < H_kv; ++kv) {
-            Group g;
-            g.cost = 0;
+            std::vector<Block> g;
             for (int b = 0; b < nblk; ++b) {
                 const int tb = b * cap;
                 const int te = std::min(nrt, tb + cap);
                 const int64_t last_row = std::min<int64_t>(packed, (int64_t)te * kRowTile) - 1;
                 const int64_t key_end = pos0 + last_row / G + 1;
-                int n_kt = 0;
-                while (n_kt < n_tiles && ptiles[n_kt].key0 < key_end)
-                    ++n_kt;
+                const int n_kt = (int)(std::partition_point(ptiles, ptiles + n_tiles,
+                                                            [&](const KTile &t) { return t.key0 < key_end; }) -
+                                       ptiles);
                 const int slot = kv * nblk + b;
                 pl.slot_end[pl.slot_base.back() + slot] =
                     n_kt ? ptiles[n_kt - 1].key0 + ptiles[n_kt - 1].n_valid : 0;
-                ItemDesc it{};
-                it.prob = pi;
-                it.kv_head = kv;
-                it.tile_begin = tb;
-                it.n_rowtiles = te - tb;
-                it.n_ktiles = n_kt;
-                it.slot = slot;
-                g.cost += (int64_t)(te - tb) * std::max(n_kt, 1);
-                g.items.push_back(it);
+                Block blk;
+                memset(&blk.it, 0, sizeof blk.it);
+                blk.it.prob = pi;
+                blk.it.kv_head = kv;
+                blk.it.tile_begin = tb;
+                blk.it.n_rowtiles = te - tb;
+                blk.it.slot = slot;
+                blk.it.opart = -1;
+                blk.n_kt = n_kt;
+                g.push_back(blk);
             }
             groups.push_back(std::move(g));
         }
     }
-    std::stable_sort(groups.begin(), groups.end(),
-                     [](const Group &x, const Group &y) { return x.cost > y.cost; });
-    constexpr int kXcd = 8;
-    std::vector<std::vector<ItemDesc>> q(kXcd);
-    std::vector<int64_t> load(kXcd, 0);
-    for (auto &g : groups) {
-        int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-        for (auto &it : g.items)
-            q[x].push_back(it);
-        load[x] += g.cost;
+
+    // Pass 1 on its own (attn_lse_kernel, two waves per SIMD) for the
+    // one-wave kernel and for any plan with key ranges; the pair kernel
+    // otherwise keeps it fused. CRKV_SWEEP1 = fused (no key ranges either) or
+    // split forces a form.
+    const char *es = getenv("CRKV_SWEEP1");
+    const bool fused_only = es && strcmp(es, "fused") == 0;
+    const bool split_anyway = es && strcmp(es, "split") == 0;
+    const int64_t step = bf16 ? step_cycles(pl.kernel, pl.rt) : 1;
+    const bool lse_anyway = bf16 && !fused_only && (pl.kernel == kBf16Wave || split_anyway);
+    if (bf16 && !fused_only && key_ranges)
+        choose_ranges(groups, step, pl.cap_rows, d, lse_anyway);
+    bool any_split = false;
+    for (auto &g : groups)
+        for (Block &b : g)
+            any_split |= b.n_ranges > 1;
+    pl.lse_kernel = lse_anyway || any_split;
+
+    // Per block: n_ranges pass-1 states of cap_rows rows; split blocks also
+    // n_ranges fp32 output partials of cap_rows x d.
+    int64_t state_f2 = 0, opart_f = 0;
+    for (auto &g : groups)
+        for (Block &b : g) {
+            b.it.state = (int32_t)state_f2;
+            if (pl.lse_kernel)
+                state_f2 += (int64_t)b.n_ranges * pl.cap_rows;
+            if (b.n_ranges > 1) {
+                b.it.opart = (int32_t)opart_f;
+                for (int t = 0; t < b.it.n_rowtiles; ++t) {
+                    OutCombItem ci{};
+                    ci.prob = b.it.prob;
+                    ci.kv_head = b.it.kv_head;
+                    ci.tile = b.it.tile_begin + t;
+                    ci.n_ranges = b.n_ranges;
+                    ci.opart = (int32_t)(opart_f + (int64_t)t * kRowTile * d);
+                    pl.comb.push_back(ci);
+                }
+                opart_f += (int64_t)b.n_ranges * pl.cap_rows * d;
+            }
+        }
+    {
+        Dealer dealer;
+        pl.model_cycles = dealer.model(groups, step);
+        dealer.emit(groups, step, pl.items);
     }
-    size_t depth = 0;
-    for (auto &v : q)
-        depth = std::max(depth, v.size());
-    ItemDesc empty{};   // n_rowtiles = 0: the workgroup exits at once
-    for (size_t d = 0; d < depth; ++d)
-        for (int x = 0; x < kXcd; ++x)
-            pl.items.push_back(d < q[x].size() ? q[x][d] : empty);
-    // trim trailing empties
-    while (!pl.items.empty() && pl.items.back().n_rowtiles == 0)
-        pl.items.pop_back();
+    for (const ItemDesc &it : pl.items)
+        if (it.n_rowtiles)
+            pl.work_cycles += (it.n_ktiles + kItemOverheadSteps) * step;
+    for (auto &g : groups)
+        for (Block &b : g) {
+            pl.split_blocks += b.n_ranges > 1;
+            pl.max_ranges = std::max(pl.max_ranges, b.n_ranges);
+        }
 
     pl.off_probs = 0;
     pl.off_items = align_up(pl.off_probs + pl.probs.size() * sizeof(ProbDesc), 256);
     pl.off_segs = align_up(pl.off_items + pl.items.size() * sizeof(ItemDesc), 256);
     pl.off_tiles = align_up(pl.off_segs + pl.segs.size() * sizeof(SegDesc), 256);
     pl.off_slots = align_up(pl.off_tiles + pl.tiles.size() * sizeof(KTile), 256);
-    pl.table_bytes = align_up(pl.off_slots + pl.slot_end.size() * sizeof(int32_t), 256);
-    pl.scratch_bytes = std::max<size_t>(partial_floats * sizeof(float), 256);
-    // The one-wave kernel's pass 1 runs as its own kernel (attn_lse_kernel,
-    // two waves per SIMD) unless CRKV_SWEEP1=fused asks for the fused form.
-    const char *es = getenv("CRKV_SWEEP1");
-    if (bf16 && pl.kernel == kBf16Wave && !(es && strcmp(es, "fused") == 0)) {
-        pl.lse_stride = cap * kRowTile;
-        pl.lse_off = align_up(pl.scratch_bytes, 256);
-        pl.scratch_bytes = pl.lse_off + pl.items.size() * (size_t)pl.lse_stride * sizeof(float);
-    }
+    pl.off_comb = align_up(pl.off_slots + pl.slot_end.size() * sizeof(int32_t), 256);
+    pl.table_bytes = align_up(pl.off_comb + pl.comb.size() * sizeof(OutCombItem), 256);
+    size_t bytes = std::max<size_t>(partial_floats * sizeof(float), 256);
+    pl.state_off = align_up(bytes, 256);
+    bytes = pl.state_off + (size_t)state_f2 * 2 * sizeof(float);
+    pl.opart_off = align_up(bytes, 256);
+    pl.scratch_bytes = pl.opart_off + (size_t)opart_f * sizeof(float);
 }
 
 // Kernel arguments of a planned launch, tables at `dev`, scratch at `scratch`.
-AttnArgs make_args(const Plan &pl, int H, int H_kv, int d, const crkv_opts &o, const unsigned char *dev,
-                   void *scratch)
+struct LaunchArgs {
+    AttnArgs attn;
+    CombineArgs comb;
+    int n_items = 0, n_comb = 0;
+    int dtype = CRKV_F32, kernel = kBf16Wave, rt = 1, d = 0;
+};
+
+LaunchArgs make_args(const Plan &pl, int H, int H_kv, int d, const crkv_opts &o, const unsigned char *dev,
+                     void *scratch)
 {
-    AttnArgs args{};
+    LaunchArgs la{};
+    AttnArgs &args = la.attn;
     args.probs = reinterpret_cast<const ProbDesc *>(dev + pl.off_probs);
     args.items = reinterpret_cast<const ItemDesc *>(dev + pl.off_items);
     args.H = H;
@@ -622,26 +890,42 @@ AttnArgs make_args(const Plan &pl, int H, int H_kv, int d, const crkv_opts &o, c
     args.G = H / H_kv;
     args.cross = o.mode == CRKV_IMPACT_CROSS_DOC ? 1 : 0;
     args.c_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-    if (pl.lse_stride) {
-        args.lse_stride = pl.lse_stride;
-        args.lse = reinterpret_cast<float *>(static_cast<unsigned char *>(scratch) + pl.lse_off);
-    }
-    return args;
+    args.cap_rows = pl.cap_rows;
+    unsigned char *sc = static_cast<unsigned char *>(scratch);
+    if (pl.lse_kernel)
+        args.state = reinterpret_cast<float *>(sc + pl.state_off);
+    if (!pl.comb.empty())
+        args.opart = reinterpret_cast<float *>(sc + pl.opart_off);
+    la.comb.probs = args.probs;
+    la.comb.items = reinterpret_cast<const OutCombItem *>(dev + pl.off_comb);
+    la.comb.opart = args.opart;
+    la.comb.G = args.G;
+    la.comb.range_stride = pl.cap_rows * d;
+    la.n_items = (int)pl.items.size();
+    la.n_comb = (int)pl.comb.size();
+    la.dtype = o.dtype;
+    la.kernel = pl.kernel;
+    la.rt = pl.rt;
+    la.d = d;
+    return la;
 }
 
-// The attention kernels of a launch: pass 1 on its own first when args.lse
-// is set, then the kernel the plan chose.
-hipError_t launch_attn_kernels(int dtype, int kernel, int rt, int d, const AttnArgs &args, int n_items,
-                               hipStream_t stream)
+// The attention kernels of a launch: pass 1 on its own first when the plan
+// runs it so, then the kernel the plan chose, then the sum of the output
+// partials of blocks split into key ranges.
+hipError_t launch_attn_kernels(const LaunchArgs &la, hipStream_t stream)
 {
+    const AttnArgs &args = la.attn;
     hipError_t e = hipSuccess;
-    if (args.lse)
-        e = launch_attn_lse(d, dtype == CRKV_KV_Q8, args, n_items, stream);
+    if (args.state)
+        e = launch_attn_lse(la.d, la.dtype == CRKV_KV_Q8, args, la.n_items, stream);
     if (e == hipSuccess)
-        e = dtype == CRKV_KV_Q8    ? launch_attn_q8(d, rt, args, n_items, stream)
-            : dtype != CRKV_BF16   ? launch_attn_f32(d, args, n_items, stream)
-            : kernel == kBf16Wave ? launch_attn_bf16_wave(d, rt, args, n_items, stream)
-                                   : launch_attn_bf16_pair(d, rt, args, n_items, stream);
+        e = la.dtype == CRKV_KV_Q8       ? launch_attn_q8(la.d, la.rt, args, la.n_items, stream)
+            : la.dtype != CRKV_BF16      ? launch_attn_f32(la.d, args, la.n_items, stream)
+            : la.kernel == kBf16Wave     ? launch_attn_bf16_wave(la.d, la.rt, args, la.n_items, stream)
+                                         : launch_attn_bf16_pair(la.d, la.rt, args, la.n_items, stream);
+    if (e == hipSuccess && la.n_comb)
+        e = launch_attn_out_combine(la.d, la.comb, la.n_comb, stream);
     return e;
 }
 
@@ -666,6 +950,7 @@ void fill_tables(Plan &pl, const crkv_problem *problems, unsigned char *host, un
     memcpy(host + pl.off_segs, pl.segs.data(), pl.segs.size() * sizeof(SegDesc));
     memcpy(host + pl.off_tiles, pl.tiles.data(), pl.tiles.size() * sizeof(KTile));
     memcpy(host + pl.off_slots, pl.slot_end.data(), pl.slot_end.size() * sizeof(int32_t));
+    memcpy(host + pl.off_comb, pl.comb.data(), pl.comb.size() * sizeof(OutCombItem));
 }
 
 crkv_opts resolve(const crkv_opts *opts)
@@ -721,16 +1006,16 @@ int check_topk_args(const float *impact, int n, int k, const int32_t *idx, int w
 hipError_t launch_planned(const Plan &pl, int n_problems, int H, int H_kv, int d, const crkv_opts &o,
                           const unsigned char *dev, void *scratch, hipStream_t stream)
 {
-    const AttnArgs args = make_args(pl, H, H_kv, d, o, dev, scratch);
+    const LaunchArgs la = make_args(pl, H, H_kv, d, o, dev, scratch);
     hipError_t e = hipSuccess;
     if (o.timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[0]), stream);
     if (e == hipSuccess)
-        e = launch_attn_kernels(o.dtype, pl.kernel, pl.rt, d, args, (int)pl.items.size(), stream);
+        e = launch_attn_kernels(la, stream);
     if (e == hipSuccess && o.timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(o.timing_events[1]), stream);
     if (e == hipSuccess)
-        e = launch_combine(args.probs, n_problems, pl.max_keys, stream);
+        e = launch_combine(la.attn.probs, n_problems, pl.max_keys, stream);
     return e;
 }
 
@@ -1109,8 +1394,8 @@ struct crkv_plan {
     int n_problems = 0;
     int d = 0;
     int dtype = CRKV_F32;
-    int kernel = kBf16Wave, rt = 1, n_items = 0, max_keys = 0;
-    AttnArgs args{};
+    int max_keys = 0;
+    LaunchArgs args{};
     unsigned char *tables = nullptr;          // device plan tables
     void *scratch = nullptr;                  // device impact partials
     bool own_scratch = false;
@@ -1199,9 +1484,6 @@ int plan_create(const crkv_problem *problems, int n_problems, int H, int H_kv, i
     p->n_problems = n_problems;
     p->d = d;
     p->dtype = o.dtype;
-    p->kernel = pl.kernel;
-    p->rt = pl.rt;
-    p->n_items = (int)pl.items.size();
     p->max_keys = pl.max_keys;
     p->topk = std::move(descs);
     p->args = make_args(pl, H, H_kv, d, o, p->tables, p->scratch);
@@ -1223,11 +1505,11 @@ int plan_launch(const crkv_plan *p, void *stream_ptr, void *const *timing_events
     if (timing_events && timing_events[0])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[0]), stream);
     if (e == hipSuccess)
-        e = launch_attn_kernels(p->dtype, p->kernel, p->rt, p->d, p->args, p->n_items, stream);
+        e = launch_attn_kernels(p->args, stream);
     if (e == hipSuccess && timing_events && timing_events[1])
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(timing_events[1]), stream);
     if (e == hipSuccess)
-        e = launch_combine(p->args.probs, p->n_problems, p->max_keys, stream);
+        e = launch_combine(p->args.attn.probs, p->n_problems, p->max_keys, stream);
     if (e == hipSuccess && !p->topk.empty()) {
         if (p->topk.size() == 1)
             e = launch_topk_one(p->topk[0], stream);
@@ -1509,6 +1791,31 @@ int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv
     return CRKV_OK;
 }
 
+int crkv_plan_stats(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                    const crkv_opts *opts, crkv_plan_stat *st)
+{
+    if (!st)
+        return fail(CRKV_E_INVAL, "crkv_plan_stats: NULL output pointer");
+    const crkv_opts o = resolve(opts);
+    const int rc = validate_batch(problems, n_problems, H, H_kv, d, o);
+    if (rc)
+        return rc;
+    Plan pl;
+    build_plan(pl, problems, n_problems, H, H_kv, d, o);
+    memset(st, 0, sizeof *st);
+    st->kernel = (o.dtype != CRKV_BF16 && o.dtype != CRKV_KV_Q8) ? 0 : pl.kernel == kBf16Wave ? 1 : 2;
+    st->row_tiles = pl.rt;
+    st->workgroups = (int)pl.items.size();
+    st->pass1_separate = pl.lse_kernel ? 1 : 0;
+    st->split_blocks = pl.split_blocks;
+    st->max_ranges = pl.max_ranges;
+    st->combine_workgroups = (int)pl.comb.size();
+    st->model_cycles = (double)pl.model_cycles;
+    st->work_cycles = (double)pl.work_cycles;
+    st->scratch_bytes = pl.scratch_bytes;
+    return CRKV_OK;
+}
+
 int crkv_attn_chunks_batched(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                              const crkv_opts *opts)
 {
@@ -1558,8 +1865,15 @@ int crkv_attn_chunks_batched_static(const crkv_problem *problems, int n_problems
                                   "opts.workspace must be NULL (pass a workspace to crkv_attn_chunks_batched)");
     Plan pl;
     build_plan(pl, problems, n_problems, H, H_kv, d, o);
-    // tables first, then the impact partials, each 256-byte aligned
-    const size_t partial_off = align_up(pl.table_bytes, 256);
+    // tables first, then the impact partials (and pass-1 states and output
+    // partials), each 256-byte aligned; a plan with key ranges whose output
+    // partials do not fit is made again without them
+    size_t partial_off = align_up(pl.table_bytes, 256);
+    if (partial_off + pl.scratch_bytes > kStaticScratchBytes && pl.split_blocks) {
+        pl = Plan();
+        build_plan(pl, problems, n_problems, H, H_kv, d, o, false);
+        partial_off = align_up(pl.table_bytes, 256);
+    }
     const size_t need = partial_off + pl.scratch_bytes;
     if (need > kStaticScratchBytes)
         return fail(CRKV_E_UNSUPPORTED,

@@ -19,7 +19,8 @@ constexpr int kRowTile = 16;       // rows per MFMA row tile
 // (8 waves per workgroup). Either way a workgroup covers kWaves * rt row tiles
 // of one KV head.
 enum Bf16Kernel { kBf16Wave = 0, kBf16Pair = 1 };
-constexpr int kWaveRowTiles[3] = {4, 5, 7};     // rt the wave kernels are built for
+constexpr int kWaveRowTiles[5] = {1, 2, 4, 5, 7};   // rt the wave kernels are built for
+constexpr int kNumWaveRowTiles = 5;
 constexpr int kWaveMaxRowTilesCross = 5;        // cross-document wave kernels: 7 would spill
 constexpr int kPairRowTiles[3] = {2, 4, 6};     // rt the pair kernels are built for
 constexpr int kQ8RowTiles[2] = {4, 5};          // rt of the wave kernel's 8-bit builds
@@ -70,15 +71,29 @@ struct ProbDesc {
     int32_t pad;
 };
 
+// A work item is one row block (up to kWaves * RT packed 16-row tiles of one
+// (problem, KV head)) over one range of its key tiles. Without a key split a
+// block is one item whose range is every key tile its last row sees; with a
+// split (one-wave-kernel plans, pass 1 in attn_lse_kernel) the block's key
+// tiles are cut into n_ranges consecutive ranges, pass 1 writes a partial
+// (max, sum) per row and range, pass 2 of each range merges them in range
+// order and, for n_ranges > 1, writes an fp32 output partial that
+// attn_out_combine_kernel sums in range order.
 struct ItemDesc {
     int32_t prob;
     int32_t kv_head;
     int32_t tile_begin;     // first packed 16-row tile (rows packed as (j, h) within the group)
     int32_t n_rowtiles;     // <= kWaves * row tiles per wave
-    int32_t n_ktiles;       // key tiles visited (prefix of the problem's list)
-    int32_t slot;           // impact partial slot within the problem
-    int32_t pad0, pad1;
+    int32_t n_ktiles;       // key tiles of this item's range
+    int32_t slot;           // impact partial slot within the problem (one per block)
+    int32_t kt_begin;       // first key tile of the range (index into the problem's list)
+    int32_t range;          // 0 .. n_ranges - 1
+    int32_t n_ranges;       // ranges of the block (1: no key split)
+    int32_t state;          // pass-1 states of the block: state[state + range * cap_rows + packed row]
+    int32_t opart;          // output partials of the block (floats), range r at + r * cap_rows * d; -1: none
+    int32_t pad;
 };
+static_assert(sizeof(ItemDesc) == 48, "work item layout");
 
 struct AttnArgs {
     const ProbDesc *probs;
@@ -86,14 +101,37 @@ struct AttnArgs {
     int32_t H, H_kv, G;
     int32_t cross;          // 1: impact skips rows of the key's own segment
     float c_log2;           // log2(e) / sqrt(d)
-    int32_t lse_stride;     // floats of `lse` per work item (pass 1 run as its own kernel)
-    float *lse;             // [item][packed row of the item's block] log2-domain row lse, or null
+    int32_t cap_rows;       // packed rows per block (kWaves * RT * 16) when pass 1 runs on its own
+    float *state;           // pass-1 (max, sum) pairs per (block, range, packed row), or null: pass 1 fused
+    float *opart;           // fp32 output partials of split blocks
+};
+
+// Output partials of split blocks summed in range order (attn_out_combine_kernel):
+// one workgroup per (split block, 16-row tile).
+struct OutCombItem {
+    int32_t prob;
+    int32_t kv_head;
+    int32_t tile;           // packed 16-row tile
+    int32_t n_ranges;
+    int32_t opart;          // floats: range 0 of the tile's first row in AttnArgs::opart
+    int32_t pad0, pad1, pad2;
+};
+static_assert(sizeof(OutCombItem) == 32, "table layout");
+
+struct CombineArgs {
+    const ProbDesc *probs;
+    const OutCombItem *items;
+    const float *opart;
+    int32_t G;
+    int32_t range_stride;   // floats between the partials of consecutive ranges (cap_rows * d)
 };
 
 // Pass 1 as its own kernel (attn_lse_kernel): kLseWaves waves per workgroup,
 // two per SIMD, the item's row tiles dealt to them round robin.
 constexpr int kLseWaves = 8;
 constexpr int kLseMaxRowTilesPerWave = 4;   // items of up to 32 row tiles
+constexpr int kCUs = 256;                   // MI355X compute units (the planner's makespan model)
+constexpr int kMinRangeTiles = 4;           // key tiles per range at least, when blocks are split
 
 // Decode step (q_len = 1): the keys of each (problem, KV head) are split into
 // ranges of key tiles; one workgroup per range writes a partial softmax state

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef short i16x4 __attribute__((__vector_size__(8)));
 typedef short i16x8 __attribute__((__vector_size__(16)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 

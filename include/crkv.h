@@ -303,6 +303,34 @@ int crkv_quantize_q8(const crkv_q8_seg *segs, int n, int H_kv, int d, const crkv
 int crkv_plan_info(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
                    const crkv_opts *opts, int *kernel, int *row_tiles, int *workgroups);
 
+/* The plan crkv_attn_chunks_batched would make for these arguments, in more
+ * detail than crkv_plan_info (host-only, for inspection and tuning):
+ * kernel, row_tiles, workgroups as there; pass1_separate = 1 when the row
+ * log-sum-exp runs as a kernel of its own before pass 2; split_blocks = row
+ * blocks whose keys are cut into ranges (max_ranges at most per block; their
+ * fp32 output partials are summed by combine_workgroups workgroups);
+ * model_cycles = the planner's modelled duration of pass 2 in shader cycles
+ * (items dealt to XCDs, one workgroup per CU) and work_cycles = the modelled
+ * work summed over items, so model_cycles * 256 / work_cycles - 1 is the
+ * modelled load imbalance; scratch_bytes = crkv_workspace_size. Returns
+ * CRKV_OK, or CRKV_E_INVAL for invalid arguments or a NULL st. */
+typedef struct crkv_plan_stat {
+    int kernel;
+    int row_tiles;
+    int workgroups;
+    int pass1_separate;
+    int split_blocks;
+    int max_ranges;
+    int combine_workgroups;
+    int pad;
+    double model_cycles;
+    double work_cycles;
+    size_t scratch_bytes;
+} crkv_plan_stat;
+
+int crkv_plan_stats(const crkv_problem *problems, int n_problems, int H, int H_kv, int d,
+                    const crkv_opts *opts, crkv_plan_stat *st);
+
 /*
  * Moving the K/V rows of selected keys (CacheBlend summary, the three-phase
  * flowchart: the K/V values of exactly the selected high-impact tokens are

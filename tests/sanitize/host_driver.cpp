@@ -21,6 +21,7 @@ struct TopkDesc;
 struct SelArgs;
 struct RopeArgs;
 struct Q8Args;
+struct CombineArgs;
 struct ProbDesc;
 [[noreturn]] static void launched(const char *what)
 {
@@ -31,6 +32,7 @@ hipError_t launch_attn_bf16_wave(int, int, const AttnArgs &, int, hipStream_t) {
 hipError_t launch_attn_bf16_pair(int, int, const AttnArgs &, int, hipStream_t) { launched("pair"); }
 hipError_t launch_attn_q8(int, int, const AttnArgs &, int, hipStream_t) { launched("q8 attention"); }
 hipError_t launch_attn_lse(int, bool, const AttnArgs &, int, hipStream_t) { launched("pass 1"); }
+hipError_t launch_attn_out_combine(int, const CombineArgs &, int, hipStream_t) { launched("output combine"); }
 hipError_t launch_decode_bf16(int, const DecodeArgs &, int, int, hipStream_t) { launched("decode"); }
 hipError_t launch_attn_f32(int, const AttnArgs &, int, hipStream_t) { launched("f32"); }
 hipError_t launch_combine(const ProbDesc *, int, int, hipStream_t) { launched("combine"); }
@@ -109,6 +111,13 @@ static void plan_round_trip(const std::vector<FakeProblem *> &ps, int H, int H_k
     EXPECT(dtype != CRKV_KV_Q8 || (kernel == 1 && (rt == 4 || rt == 5)));
     EXPECT(rt >= 1 && wg >= 1);
     EXPECT(crkv_workspace_size(arr.data(), (int)arr.size(), H, H_kv, d, &o) > 0);
+    crkv_plan_stat st;
+    EXPECT(crkv_plan_stats(arr.data(), (int)arr.size(), H, H_kv, d, &o, &st) == CRKV_OK);
+    EXPECT(st.kernel == kernel && st.row_tiles == rt && st.workgroups == wg);
+    EXPECT(st.scratch_bytes == crkv_workspace_size(arr.data(), (int)arr.size(), H, H_kv, d, &o));
+    EXPECT(st.max_ranges >= 1 && (st.split_blocks == 0) == (st.combine_workgroups == 0));
+    EXPECT(st.split_blocks == 0 || st.pass1_separate == 1);
+    EXPECT(dtype == CRKV_F32 || st.model_cycles > 0);
     if (dtype == CRKV_BF16 && mode == CRKV_IMPACT_QUERY_ROWS) {
         bool q1 = true;
         for (auto *p : ps)
@@ -282,6 +291,23 @@ int main()
             }
         unsetenv("CRKV_BF16_KERNEL");
         unsetenv("CRKV_ROW_TILES");
+        // key ranges: none, forced counts (more ranges than key tiles too), pass-1 forms
+        const char *splits[4] = {"off", "2", "7", "100000"};
+        for (const char *sp : splits) {
+            setenv("CRKV_KEY_SPLIT", sp, 1);
+            plan_round_trip(rgp, 64, 8, 128, CRKV_BF16, CRKV_IMPACT_QUERY_ROWS);
+            plan_round_trip({&cd}, 32, 32, 128, CRKV_BF16, CRKV_IMPACT_CROSS_DOC);
+            plan_round_trip({&e1, &e2, &e3}, 8, 2, 128, CRKV_BF16, CRKV_IMPACT_QUERY_ROWS);
+            plan_round_trip(l3p, 32, 8, 128, CRKV_KV_Q8, CRKV_IMPACT_QUERY_ROWS);
+        }
+        unsetenv("CRKV_KEY_SPLIT");
+        const char *sweeps[2] = {"fused", "split"};
+        for (const char *sw : sweeps) {
+            setenv("CRKV_SWEEP1", sw, 1);
+            plan_round_trip(rgp, 64, 8, 128, CRKV_BF16, CRKV_IMPACT_QUERY_ROWS);
+            plan_round_trip({&l2}, 32, 32, 128, CRKV_BF16, CRKV_IMPACT_QUERY_ROWS);
+        }
+        unsetenv("CRKV_SWEEP1");
     }
     if (g_fail) {
         std::fprintf(stderr, "%d expectations failed\n", g_fail);

@@ -8,6 +8,7 @@ import re
 import pytest
 
 import attention_precomputed_chunk_amd as crkv
+import workloads
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "crkv.h")
 
@@ -149,9 +150,11 @@ def test_plan_info_picks_kernel_by_shape(monkeypatch):
     (4 x 7 tiles); thousands of rows go to the wave-pair kernel."""
     monkeypatch.delenv("CRKV_BF16_KERNEL", raising=False)
     monkeypatch.delenv("CRKV_ROW_TILES", raising=False)
+    monkeypatch.setenv("CRKV_KEY_SPLIT", "off")
     few = [_fake_problem([2500] * 4, 100, 32, 128) for _ in range(4)]
     p = crkv.crkv_plan_info(few, 32, 8, 128, mode="query", dtype=crkv.CRKV_BF16)
     assert p == {"kernel": "bf16_wave", "row_tiles": 7, "workgroups": 4 * 8}
+    monkeypatch.delenv("CRKV_KEY_SPLIT")
     many = [_fake_problem([3000, 3000], 1000, 64, 128)]
     p = crkv.crkv_plan_info(many, 64, 8, 128, mode="query", dtype=crkv.CRKV_BF16)
     assert p["kernel"] == "bf16_pair" and p["row_tiles"] == 6
@@ -161,6 +164,53 @@ def test_plan_info_picks_kernel_by_shape(monkeypatch):
     monkeypatch.setenv("CRKV_ROW_TILES", "5")
     p = crkv.crkv_plan_info(many, 64, 8, 128, mode="cross", dtype=crkv.CRKV_BF16)
     assert p["kernel"] == "bf16_wave" and p["row_tiles"] == 5
+
+
+def _stats(probs, H, H_kv, mode="query"):
+    return crkv.crkv_plan_stats(probs, H, H_kv, 128, mode=mode, dtype=crkv.CRKV_BF16)
+
+
+def test_key_ranges_planned_where_the_model_gains(monkeypatch):
+    """Host-only planner checks of the key-range split: a single short-query
+    layer (32 row blocks on 256 CUs) is cut into ranges and its output rows
+    summed by the combine; 256 equal blocks (the 32-layer GQA launch) are not;
+    the ragged batch's modelled imbalance drops below 5 %; a forced count
+    cuts every block (at most one range per key tile); the fused pass 1
+    plans no ranges."""
+    for v in ("CRKV_BF16_KERNEL", "CRKV_ROW_TILES", "CRKV_KEY_SPLIT", "CRKV_SWEEP1"):
+        monkeypatch.delenv(v, raising=False)
+    layer = [_fake_problem([512] * 4, 64, 32, 128)]
+    st = _stats(layer, 32, 32)
+    assert st["kernel"] == "bf16_wave" and st["row_tiles"] == 1 and st["pass1_separate"] == 1
+    assert st["split_blocks"] == 32 and st["max_ranges"] >= 4
+    assert st["combine_workgroups"] == 32 * 4        # 64 rows of each head: 4 row tiles
+    assert st["workgroups"] >= 32 * st["max_ranges"] - 8
+    assert st["imbalance"] < 0.1
+    assert crkv.crkv_workspace_size(layer, 32, 32, 128, dtype=crkv.CRKV_BF16) == st["scratch_bytes"]
+
+    layers = [_fake_problem([2500] * 4, 100, 32, 128) for _ in range(32)]
+    st = _stats(layers, 32, 8)
+    assert st["split_blocks"] == 0 and st["workgroups"] == 256 and st["imbalance"] < 1e-9
+
+    lens, qs = workloads.ragged_shapes(workloads.CONFIGS["ragged_70b"])
+    ragged = [_fake_problem(ln, q, 64, 128) for ln, q in zip(lens, qs)]
+    monkeypatch.setenv("CRKV_KEY_SPLIT", "off")
+    whole = _stats(ragged, 64, 8)
+    monkeypatch.delenv("CRKV_KEY_SPLIT")
+    st = _stats(ragged, 64, 8)
+    assert st["imbalance"] < 0.05 < whole["imbalance"]
+    assert st["model_cycles"] < whole["model_cycles"]
+
+    monkeypatch.setenv("CRKV_KEY_SPLIT", "3")
+    st = _stats(layers[:2], 32, 8)
+    assert st["split_blocks"] == 16 and st["max_ranges"] == 3 and st["workgroups"] == 48
+    monkeypatch.setenv("CRKV_KEY_SPLIT", "5")
+    tiny = [_fake_problem([40], 8, 4, 128)]           # key tiles of 32 + 8 and 8 keys: at most 3 ranges
+    st = _stats(tiny, 4, 4)
+    assert st["max_ranges"] == 3
+    monkeypatch.setenv("CRKV_SWEEP1", "fused")
+    st = _stats(layers[:2], 32, 8)
+    assert st["split_blocks"] == 0 and st["pass1_separate"] == 0
 
 
 def test_plan_info_rejects_invalid():

@@ -92,7 +92,8 @@ def test_small_shapes(case):
 
 # Every built bf16 (kernel, row tiles) configuration, forced through the
 # planner's override, on shapes whose rows span several workgroups.
-FORCED_BUILDS = [("wave", 4), ("wave", 5), ("wave", 7), ("pair", 2), ("pair", 4), ("pair", 6)]
+FORCED_BUILDS = [("wave", 1), ("wave", 2), ("wave", 4), ("wave", 5), ("wave", 7), ("pair", 2), ("pair", 4),
+                 ("pair", 6)]
 FORCED_CASES = [2, 3, 4, 5, 8]   # indices into SMALL: GQA query rows, cross (d=128, d=64), all rows, G=8
 
 
@@ -131,6 +132,72 @@ def test_wave_pass1_forms(case, rt, sweep1, monkeypatch):
     run_and_compare(wl, label="pass1-%s-wave%d-small%d" % (sweep1, rt, case))
 
 
+# Row blocks cut into key ranges: pass 1 writes one (max, sum) state per
+# range, pass 2 of every range merges them and writes fp32 output partials,
+# the combine sums them. Forced range counts (100000: one range per key
+# tile) on every build, and the pair kernel reading a separate pass 1
+# without ranges.
+SPLIT_BUILDS = [("wave", 1), ("wave", 2), ("wave", 4), ("wave", 7), ("pair", 2), ("pair", 6)]
+
+
+@pytest.mark.parametrize("split", ["2", "3", "100000"])
+@pytest.mark.parametrize("build", SPLIT_BUILDS, ids=["%s%d" % b for b in SPLIT_BUILDS])
+@pytest.mark.parametrize("case", [0, 2, 3, 5, 8])
+def test_key_ranges(case, build, split, monkeypatch):
+    seed, doc, q, H, H_kv, d, dtype, mode = SMALL[case]
+    kernel, rt = build
+    if kernel == "wave" and mode == "cross" and rt > 5:
+        pytest.skip("no cross-document wave build with 7 row tiles")
+    monkeypatch.setenv("CRKV_BF16_KERNEL", kernel)
+    monkeypatch.setenv("CRKV_ROW_TILES", str(rt))
+    monkeypatch.setenv("CRKV_KEY_SPLIT", split)
+    say("key ranges", split, kernel, rt, "small case", SMALL[case])
+    wl = workloads.custom(100 + seed, doc, q, H, H_kv, d, dtype=dtype, mode=mode, r=0.1, n_problems=2)
+    dw = DeviceWorkload(wl)
+    st = crkv.crkv_plan_stats(dw.problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    assert st["kernel"] == "bf16_" + kernel and st["row_tiles"] == rt and st["split_blocks"] > 0, st
+    assert st["pass1_separate"] == 1 and st["max_ranges"] >= 2
+    run_and_compare(wl, label="ranges%s-%s%d-small%d" % (split, kernel, rt, case))
+
+
+@pytest.mark.parametrize("rt", [2, 4, 6])
+@pytest.mark.parametrize("case", [2, 3, 8])
+def test_pair_separate_pass1(case, rt, monkeypatch):
+    seed, doc, q, H, H_kv, d, dtype, mode = SMALL[case]
+    monkeypatch.setenv("CRKV_BF16_KERNEL", "pair")
+    monkeypatch.setenv("CRKV_ROW_TILES", str(rt))
+    monkeypatch.setenv("CRKV_KEY_SPLIT", "off")
+    monkeypatch.setenv("CRKV_SWEEP1", "split")
+    say("pair, separate pass 1", rt, "small case", SMALL[case])
+    wl = workloads.custom(100 + seed, doc, q, H, H_kv, d, dtype=dtype, mode=mode, r=0.1, n_problems=2)
+    dw = DeviceWorkload(wl)
+    st = crkv.crkv_plan_stats(dw.problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    assert st["pass1_separate"] == 1 and st["split_blocks"] == 0, st
+    run_and_compare(wl, label="pair%d-sep-small%d" % (rt, case))
+
+
+def test_key_ranges_repeat_bit_identical(monkeypatch):
+    """A split plan (the planner's own: one short-query MHA layer, whose 32
+    row blocks are cut into ranges) gives the same bits on every call."""
+    for v in ("CRKV_BF16_KERNEL", "CRKV_ROW_TILES", "CRKV_KEY_SPLIT", "CRKV_SWEEP1"):
+        monkeypatch.delenv(v, raising=False)
+    wl = workloads.custom(23, [512, 512, 512, 512], 64, 32, 32, 128, dtype="bf16", n_problems=1, k_outliers=4)
+    dw = DeviceWorkload(wl)
+    st = crkv.crkv_plan_stats(dw.problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    assert st["split_blocks"] == 32, st
+    dw.attn()
+    torch.cuda.synchronize()
+    o1 = dw.problems[0]["out"].clone()
+    i1 = dw.problems[0]["impact"].clone()
+    for _ in range(3):
+        dw.problems[0]["out"].zero_()
+        dw.problems[0]["impact"].zero_()
+        dw.attn()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.problems[0]["out"], o1)
+        assert torch.equal(dw.problems[0]["impact"], i1)
+
+
 def rising_scores_workload(seed, mode):
     """Scores that climb by about 80 log2 units along the keys: channel 0 of
     every key grows with its position and channel 0 of every query row is
@@ -152,16 +219,23 @@ def rising_scores_workload(seed, mode):
     return wl
 
 
-@pytest.mark.parametrize("build", [None, ("wave", 4), ("wave", 7), ("pair", 6), ("wave", 7, "fused")],
-                         ids=["planner", "wave4", "wave7", "pair6", "wave7-fused"])
+RISING_BUILDS = [None, ("wave", 4), ("wave", 7), ("pair", 6), ("wave", 7, "fused"), ("wave", 4, "3"),
+                 ("pair", 6, "3")]
+
+
+@pytest.mark.parametrize("build", RISING_BUILDS,
+                         ids=["planner", "wave4", "wave7", "pair6", "wave7-fused", "wave4-ranges3", "pair6-ranges3"])
 def test_rising_scores(build, monkeypatch):
     """Sweep 1's exact-maximum path taken again and again (a row's maximum
-    keeps rising), against the oracle."""
+    keeps rising), against the oracle; also with the keys cut into ranges
+    (each range's state starts from its own first tile)."""
     if build:
         monkeypatch.setenv("CRKV_BF16_KERNEL", build[0])
         monkeypatch.setenv("CRKV_ROW_TILES", str(build[1]))
-        if len(build) > 2:
+        if len(build) > 2 and build[2] == "fused":
             monkeypatch.setenv("CRKV_SWEEP1", build[2])
+        elif len(build) > 2:
+            monkeypatch.setenv("CRKV_KEY_SPLIT", build[2])
     say("rising scores", build)
     run_and_compare(rising_scores_workload(350, "query"), label="rising-%s" % (build,))
 

@@ -138,10 +138,13 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("rt", [None, 4, 5], ids=["planner", "rt4", "rt5"])
+@pytest.mark.parametrize("rt", [None, 4, 5, "4/3"], ids=["planner", "rt4", "rt5", "rt4-ranges3"])
 @pytest.mark.parametrize("case", range(len(SMALL)))
 def test_q8_prefill_small(case, rt, monkeypatch):
     seed, doc, q, H, H_kv, d, mode, ko = SMALL[case]
+    if rt == "4/3":   # keys cut into 3 ranges per row block
+        rt = 4
+        monkeypatch.setenv("CRKV_KEY_SPLIT", "3")
     if rt:
         monkeypatch.setenv("CRKV_ROW_TILES", str(rt))
     say("q8 prefill case", SMALL[case], "rt", rt)

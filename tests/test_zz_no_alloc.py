@@ -46,11 +46,15 @@ CASES = [
     ("gqa-query", 501, [700, 0, 333, 64], 90, 16, 4, 128, "bf16", "query", 6),
     ("cross", 502, [257, 129, 64], 40, 8, 8, 128, "bf16", "cross", 3),
     ("f32", 503, [130, 67], 21, 4, 2, 64, "f32", "query", 2),
+    # one short-query MHA layer: the planner cuts its 32 row blocks into key
+    # ranges (pass-1 states and output partials in the static scratch too)
+    ("mha-ranges", 504, [512, 512, 512, 512], 64, 32, 32, 128, "bf16", "query", 1),
 ]
 SMALLER = {
     "gqa-query": (511, [200, 31], 17, 3),
     "cross": (512, [65, 40], 9, 1),
     "f32": (513, [33], 5, 1),
+    "mha-ranges": (514, [300, 200], 30, 1),
 }
 
 
@@ -60,6 +64,9 @@ def test_static_matches_per_call_twice(case):
     s2, doc2, q2, n2 = SMALLER[label]
     big = workloads.custom(seed, doc, q, H, H_kv, d, dtype=dtype, mode=mode, r=0.1, n_problems=n)
     small = workloads.custom(s2, doc2, q2, H, H_kv, d, dtype=dtype, mode=mode, r=0.1, n_problems=n2)
+    if label == "mha-ranges":
+        st = crkv.crkv_plan_stats(DeviceWorkload(big).problems, H, H_kv, d, mode=mode)
+        assert st["split_blocks"] > 0, st
     for step, wl in enumerate((big, small, big)):
         say("static scratch: %s call %d (%d problems, docs %s)" % (label, step, len(wl.problems),
                                                                   wl.problems[0].lens[:-1]))
