@@ -501,6 +501,12 @@ constexpr int64_t kItemOverheadSteps = 2;   // Q load, lse, epilogue of a workgr
 constexpr int64_t kLaunchCycles = 8000;     // one more kernel in the stream (about 3.5 us)
 constexpr int64_t kBytesPerCycle = 1800;    // HBM bytes per shader cycle, streaming (about 4 TB/s)
 
+bool item_order_lpt()
+{
+    const char *e = getenv("CRKV_ITEM_ORDER");
+    return !(e && strcmp(e, "group") == 0);
+}
+
 // Key tiles of range r of a block cut into n ranges of nearly equal length.
 inline int range_begin(int n_kt, int n, int r) { return (int)((int64_t)r * n_kt / n); }
 
@@ -513,6 +519,7 @@ inline int range_begin(int n_kt, int n, int r) { return (int)((int64_t)r * n_kt 
 // in that order on whichever of its CUs frees first (one workgroup per CU),
 // each taking (key tiles + fixed part) steps of `step` cycles.
 struct Dealer {
+    bool lpt = true;   // false: each group's items together, its longest first (CRKV_ITEM_ORDER=group)
     std::vector<std::pair<int64_t, int>> order;   // (cost, group)
     std::vector<int> xcd;                         // per group
     std::vector<int32_t> n_kt[kXcd];              // per XCD: key tiles of its items
@@ -546,14 +553,19 @@ struct Dealer {
         assign(groups, step);
         for (auto &v : n_kt)
             v.clear();
-        for (const auto &o : order)
+        for (const auto &o : order) {
+            auto &v = n_kt[xcd[o.second]];
+            const size_t first = v.size();
             for (const Block &b : groups[o.second])
                 for (int r = 0; r < b.n_ranges; ++r)
-                    n_kt[xcd[o.second]].push_back(range_begin(b.n_kt, b.n_ranges, r + 1) -
-                                                  range_begin(b.n_kt, b.n_ranges, r));
+                    v.push_back(range_begin(b.n_kt, b.n_ranges, r + 1) - range_begin(b.n_kt, b.n_ranges, r));
+            if (!lpt)
+                std::sort(v.begin() + first, v.end(), std::greater<int32_t>());
+        }
         int64_t makespan = 0;
         for (auto &v : n_kt) {
-            std::sort(v.begin(), v.end(), std::greater<int32_t>());
+            if (lpt)
+                std::sort(v.begin(), v.end(), std::greater<int32_t>());
             cu.assign(kCUsPerXcd, 0);   // min-heap of the CUs' free times
             for (int32_t n : v) {
                 std::pop_heap(cu.begin(), cu.end(), std::greater<int64_t>());
@@ -570,7 +582,10 @@ struct Dealer {
     {
         assign(groups, step);
         std::vector<std::vector<ItemDesc>> q(kXcd);
-        for (const auto &o : order)
+        auto longer = [](const ItemDesc &x, const ItemDesc &y) { return x.n_ktiles > y.n_ktiles; };
+        for (const auto &o : order) {
+            auto &v = q[xcd[o.second]];
+            const size_t first = v.size();
             for (const Block &b : groups[o.second])
                 for (int r = 0; r < b.n_ranges; ++r) {
                     ItemDesc it = b.it;
@@ -578,12 +593,15 @@ struct Dealer {
                     it.n_ktiles = range_begin(b.n_kt, b.n_ranges, r + 1) - it.kt_begin;
                     it.range = r;
                     it.n_ranges = b.n_ranges;
-                    q[xcd[o.second]].push_back(it);
+                    v.push_back(it);
                 }
+            if (!lpt)
+                std::stable_sort(v.begin() + first, v.end(), longer);
+        }
         size_t depth = 0;
         for (auto &v : q) {
-            std::stable_sort(v.begin(), v.end(),
-                             [](const ItemDesc &x, const ItemDesc &y) { return x.n_ktiles > y.n_ktiles; });
+            if (lpt)
+                std::stable_sort(v.begin(), v.end(), longer);
             depth = std::max(depth, v.size());
         }
         ItemDesc empty{};   // n_rowtiles = 0: the workgroup exits at once
@@ -625,7 +643,7 @@ void choose_ranges(Groups &groups, int64_t step, int cap_rows, int d, bool lse_k
     sig.reserve(4 + 2 * groups.size() * (groups.empty() ? 0 : groups[0].size()));
     sig.push_back(step);
     sig.push_back(d);
-    sig.push_back(lse_kernel_anyway);
+    sig.push_back(lse_kernel_anyway + 2 * item_order_lpt());
     sig.push_back((int64_t)groups.size());
     for (auto &g : groups) {
         sig.push_back(-(int64_t)g.size());
@@ -652,6 +670,7 @@ void choose_ranges(Groups &groups, int64_t step, int cap_rows, int d, bool lse_k
         memo.emplace(std::move(sig), r);
     };
     static thread_local Dealer dealer;
+    dealer.lpt = item_order_lpt();
     int64_t work = 0;
     for (auto &g : groups)
         for (const Block &b : g)
@@ -844,6 +863,7 @@ void build_plan(Plan &pl, const crkv_problem *problems, int n_problems, int H, i
         }
     {
         Dealer dealer;
+        dealer.lpt = item_order_lpt();
         pl.model_cycles = dealer.model(groups, step);
         dealer.emit(groups, step, pl.items);
     }

@@ -9,10 +9,10 @@
 // first histogram is spread over many bins even when all values have the same
 // sign and a narrow exponent range. Histograms are private per wave to keep
 // LDS atomic contention low. Every key above T is taken; of the keys equal to
-// T the lowest indices are taken (an ordered scan over contiguous index
-// ranges, one per thread). The k winners are sorted by (key descending, index
-// ascending) with a bitonic network in LDS, packed as 64-bit words
-// (key << 32 | ~index) so that one descending sort gives both orders.
+// T the lowest indices are taken. The k winners are written in index order
+// and sorted by key, descending, with a stable LSD radix sort over the bits
+// where they differ, which leaves equal keys in index order: the output is
+// ordered by (value descending, index ascending).
 #include <hip/hip_runtime.h>
 
 #include "crkv_internal.h"
@@ -49,15 +49,15 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int *wave_tot)
     return x + before;
 }
 
-__device__ void topk_body(const TopkDesc td)
+__device__ __forceinline__ void topk_body(const TopkDesc td)
 {
-    __shared__ uint32_t keys[kTopkLdsKeys];
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kTopkLdsKeys];   // then the sort's second buffer
     __shared__ uint32_t whist[kTopkWaves][256];
-    __shared__ unsigned long long sel[kTopkMaxK];
+    __shared__ __attribute__((aligned(16))) unsigned long long sel[kTopkMaxK];
     __shared__ int wave_tot[kTopkWaves];
     __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
     __shared__ uint32_t s_digit;
-    __shared__ int s_above, s_gt;
+    __shared__ int s_above;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = td.n, k = td.k;
@@ -148,92 +148,103 @@ __device__ void topk_body(const TopkDesc td)
         __syncthreads();
     }
     const uint32_t T = prefix;
-    const int n_gt = k - remaining;   // keys strictly above T: all taken
 
-    // ordered selection of the ties: thread t scans indices [t*chunk, ...)
+    // The k winners in index order: thread t scans indices [t*chunk, ...),
+    // counting keys above T and keys equal to T; scans of both counts place
+    // every winner and decide which ties are taken (the first `remaining` in
+    // index order).
     const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
     const int b = min(n, tid * chunk), e = min(n, b + chunk);
-    int eq = 0;
-    for (int i = b; i < e; ++i)
-        eq += key_at(i) == T ? 1 : 0;
-    if (tid == 0)
-        s_gt = 0;
-    int rank = block_inclusive_scan(eq, wave_tot) - eq;
+    int gt = 0, eq = 0;
     for (int i = b; i < e; ++i) {
         const uint32_t kk = key_at(i);
-        const unsigned long long packed =
-            ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
-        if (kk > T) {
-            sel[atomicAdd(&s_gt, 1)] = packed;   // any order: the sort orders them
-        } else if (kk == T) {
-            if (rank < remaining)
-                sel[n_gt + rank] = packed;
-            ++rank;
+        gt += kk > T ? 1 : 0;
+        eq += kk == T ? 1 : 0;
+    }
+    const int gt_before = block_inclusive_scan(gt, wave_tot) - gt;
+    const int eq_before = block_inclusive_scan(eq, wave_tot) - eq;
+    int taken = min(eq_before, remaining);   // ties taken before this thread's chunk
+    int pos = gt_before + taken;
+    for (int i = b; i < e; ++i) {
+        const uint32_t kk = key_at(i);
+        if (kk > T || (kk == T && taken < remaining)) {
+            sel[pos++] = ((unsigned long long)kk << 32) | (unsigned int)i;
+            taken += kk == T ? 1 : 0;
         }
     }
-    int P = 128;   // at least one 128-entry block (see the sort)
-    while (P < k)
-        P <<= 1;
-    for (int i = k + tid; i < P; i += kTopkThreads)
-        sel[i] = 0ull;   // below every real entry
     __syncthreads();
 
-    // Bitonic sort, descending, of P = 2^j >= 128 entries. Stages whose
-    // stride is at least 128 compare entries of different 128-entry blocks
-    // and go through LDS with a barrier each. The others stay inside a block:
-    // wave w holds block w (and w + 16, ...) in registers, lane l entries l
-    // and l + 64, and such a run of stages is done with lane shuffles and no
-    // LDS traffic.
-    auto reg_run = [&](int size_lo, int size_hi, int stride_first) {
-        for (int blk = wave; blk < P / 128; blk += kTopkWaves) {
-            const int base = blk * 128;
-            unsigned long long x0 = sel[base + lane], x1 = sel[base + lane + 64];
-            const int i0 = base + lane, i1 = i0 + 64;
-            for (int size = size_lo; size <= size_hi; size <<= 1) {
-                for (int stride = (size == size_lo ? stride_first : size >> 1); stride > 0; stride >>= 1) {
-                    if (stride == 64) {   // pair (i0, i1) of this lane
-                        const bool desc = (i0 & size) == 0;
-                        if ((x0 < x1) == desc) {
-                            const unsigned long long t = x0;
-                            x0 = x1;
-                            x1 = t;
-                        }
-                    } else {
-                        const unsigned long long y0 = __shfl_xor(x0, stride), y1 = __shfl_xor(x1, stride);
-                        const bool lo = (lane & stride) == 0;
-                        // the lower position of a pair keeps the larger entry in a descending block
-                        const bool max0 = lo == ((i0 & size) == 0), max1 = lo == ((i1 & size) == 0);
-                        x0 = max0 ? (x0 > y0 ? x0 : y0) : (x0 < y0 ? x0 : y0);
-                        x1 = max1 ? (x1 > y1 ? x1 : y1) : (x1 < y1 ? x1 : y1);
-                    }
+    // Stable LSD radix sort of the k winners by key, descending (bin = 255 -
+    // digit), over the 8-bit digits below the common prefix of the largest
+    // key and T; equal keys keep index order. Wave w ranks the entries
+    // [w*S, (w+1)*S) in rounds of 64: within a round the lanes holding the
+    // same digit find each other with 8 ballots, and a wave-private count per
+    // bin carries the rank across rounds. The counts then become each
+    // (bin, wave)'s first slot, in bin order then wave order, and every entry
+    // moves there. The sort ping-pongs between sel and `keys`, free once the
+    // winners are picked (8192 64-bit entries either way).
+    unsigned long long *src = sel;
+    unsigned long long *dst = reinterpret_cast<unsigned long long *>(keys);
+    const int sig = (T == mx) ? 0 : 32 - __clz((int)(T ^ mx));   // bits that differ among the winners
+    const int S = ((k + kTopkWaves - 1) / kTopkWaves + 63) / 64 * 64;   // entries per wave
+    const int rounds = S / 64;   // <= kTopkMaxK / kTopkWaves / 64 = 8
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int shift = 0; shift < sig; shift += 8) {
+        for (int q = lane; q < 256; q += 64)
+            whist[wave][q] = 0;
+        unsigned long long ent[kTopkMaxK / kTopkWaves / 64];
+        int bin[kTopkMaxK / kTopkWaves / 64], rank[kTopkMaxK / kTopkWaves / 64];
+#pragma unroll
+        for (int r = 0; r < kTopkMaxK / kTopkWaves / 64; ++r) {
+            if (r < rounds) {   // wave-uniform
+                const int i = wave * S + r * 64 + lane;
+                const bool valid = i < k;
+                ent[r] = valid ? src[i] : 0ull;
+                bin[r] = 255 - (int)((ent[r] >> (32 + shift)) & 255u);
+                unsigned long long peers = __ballot(valid);
+#pragma unroll
+                for (int bit = 0; bit < 8; ++bit) {
+                    const unsigned long long on = __ballot((bin[r] >> bit) & 1);
+                    peers &= ((bin[r] >> bit) & 1) ? on : ~on;
                 }
+                const int before = __popcll(peers & below);
+                rank[r] = (int)whist[wave][bin[r]] + before;   // read by every lane before the leader adds
+                if (valid && (peers >> lane) == 1ull)      // the highest lane of its digit group
+                    whist[wave][bin[r]] += (uint32_t)(before + 1);
             }
-            sel[base + lane] = x0;
-            sel[base + lane + 64] = x1;
         }
         __syncthreads();
-    };
-    reg_run(2, 128, 1);   // every stage of the sizes up to 128
-    for (int size = 256; size <= P; size <<= 1) {
-        int stride = size >> 1;
-        for (; stride >= 128; stride >>= 1) {
-            for (int t = tid; t < P / 2; t += kTopkThreads) {
-                const int lo = 2 * t - (t & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const unsigned long long x = sel[lo], y = sel[hi];
-                if ((x < y) == desc) {
-                    sel[lo] = y;
-                    sel[hi] = x;
-                }
-            }
-            __syncthreads();
+        // (bin, wave) -> first slot: bins in order, waves in order within a bin
+        int tot = 0;
+        uint32_t c[kTopkWaves];
+        if (tid < 256) {
+#pragma unroll
+            for (int w = 0; w < kTopkWaves; ++w)
+                c[w] = whist[w][tid];
+#pragma unroll
+            for (int w = 0; w < kTopkWaves; ++w)
+                tot += (int)c[w];
         }
-        reg_run(size, size, 64);
+        int base = block_inclusive_scan(tot, wave_tot) - tot;
+        if (tid < 256) {
+#pragma unroll
+            for (int w = 0; w < kTopkWaves; ++w) {
+                whist[w][tid] = (uint32_t)base;
+                base += (int)c[w];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kTopkMaxK / kTopkWaves / 64; ++r)
+            if (r < rounds && wave * S + r * 64 + lane < k)
+                dst[whist[wave][bin[r]] + rank[r]] = ent[r];
+        __syncthreads();
+        unsigned long long *t = src;
+        src = dst;
+        dst = t;
     }
-    __syncthreads();
     for (int i = tid; i < k; i += kTopkThreads)
-        td.idx[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(sel[i] & 0xFFFFFFFFull));
+        td.idx[i] = (int32_t)(src[i] & 0xFFFFFFFFull);
 }
 
 __global__ void __launch_bounds__(kTopkThreads) topk_one_kernel(const TopkDesc td) { topk_body(td); }

@@ -101,7 +101,7 @@ def algorithmic_work(wl):
 # Sources each timed kernel is built from; a counter summary stays valid while
 # their hash matches.
 KERNEL_SOURCES = {
-    "attn": ("attn_bf16_wave.hip", "attn_bf16_pair.hip", "attn_bf16_common.h", "device_util.h",
+    "attn": ("attn_bf16_wave.hip", "attn_bf16_pair.hip", "attn_lse.hip", "attn_bf16_common.h", "device_util.h",
              "crkv_internal.h", "crkv_api.hip"),
     "decode": ("decode_bf16.hip", "attn_bf16_common.h", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
     "kvsel": ("kvsel.hip", "device_util.h", "crkv_internal.h", "crkv_api.hip"),
@@ -576,7 +576,7 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
     if wl.spec.decode:
         plan = {"kernel": "decode_split+merge", "row_tiles": 1, "workgroups": None}
     else:
-        plan = crkv.crkv_plan_info(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode, dtype=dtype)
+        plan = crkv.crkv_plan_stats(problems, wl.H, wl.H_kv, wl.d, mode=wl.mode, dtype=dtype)
     log("plan: %s" % plan)
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
@@ -626,6 +626,16 @@ def bench_attention(args, torch, crkv, workloads, name, steps, warmup, with_cpu)
            "workgroups": plan["workgroups"],
            "kernel_ms": round(k_ms, 4), "kernel_ms_p50": round(p50, 4), "kernel_ms_p10": round(p10, 4),
            "kernel_ms_p90": round(p90, 4), "alg_bytes_per_launch": nbytes}
+    if not decode:
+        # the timed region holds every attention kernel of the launch
+        # (kernel_ms is their sum): pass 1 on its own where the plan runs it
+        # so, pass 2, and the sum of output partials where blocks are cut
+        # into key ranges
+        hbm["kernels"] = ((["attn_lse_kernel"] if plan["pass1_separate"] else []) + [hbm["kernel"]] +
+                          (["attn_out_combine_kernel"] if plan["split_blocks"] else []))
+        hbm["split_blocks"] = plan["split_blocks"]
+        hbm["max_ranges"] = plan["max_ranges"]
+        hbm["model_imbalance"] = round(plan["imbalance"], 4)
     mfma = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": round(achieved_tf / mfma_peak, 4),
             "alg_flops_per_launch": flops, "visible_pairs": npairs,

@@ -407,6 +407,8 @@ def test_partition_of_keys_into_chunks():
     (1, 1, "normal"), (8, 8, "normal"), (1000, 1, "normal"), (10000, 1500, "normal"),
     (16384, 1638, "normal"), (5000, 700, "ties"), (5000, 4999, "ties"), (777, 300, "signed_zeros"),
     (100000, 8192, "normal"), (4096, 409, "constant"), (3000, 17, "negative"),
+    (20000, 8192, "ties"), (16385, 2, "normal"), (50, 50, "ties"), (12000, 8192, "wide"), (10000, 1500, "wide"),
+    (8192, 409, "wide"),
 ])
 def test_topk_bit_exact(n, k, kind):
     rng = np.random.default_rng(n * 31 + k)
@@ -418,6 +420,8 @@ def test_topk_bit_exact(n, k, kind):
         v = rng.choice(np.array([-0.0, 0.0, 1e-30, -1e-30, 2.0], dtype=np.float32), size=n)
     elif kind == "constant":
         v = np.full(n, 0.37, dtype=np.float32)
+    elif kind == "wide":   # positive, over some 40 binades (impact-like)
+        v = np.exp(4.0 * rng.standard_normal(n)).astype(np.float32)
     else:
         v = -np.abs(rng.standard_normal(n)).astype(np.float32)
     ref = oracle.topk(v, k)
