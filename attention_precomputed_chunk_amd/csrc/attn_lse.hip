@@ -154,34 +154,51 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
         else
             stg.store(st, lds_k[buf], nullptr);
     };
-    // Descriptors two tiles ahead, data one tile ahead, K double-buffered in
-    // LDS (deeper register prefetch and a software-pipelined form that scored
-    // the next row tile under this one's exponentials both measured slower
-    // on the 32-layer workload: the waves then waited longer at the barrier).
+    // Two key tiles per barrier: step g scores tiles 2g and 2g + 1 from one
+    // pair of LDS buffers while tiles 2g + 2 and 2g + 3 are loaded into
+    // registers and then stored into the other pair; descriptors run two
+    // tiles further ahead. (One tile per barrier left each step's load
+    // latency and barrier exposed; deeper register prefetch and a software-
+    // pipelined form that scored the next row tile under this one's
+    // exponentials measured slower.)
     auto desc = [&](int tt) { return load_tile(pr.tiles, kt0 + min(tt, n_kt - 1), lane); };
-    TileSR cur = to_sr(desc(0));
-    uint32_t nraw = desc(1);
-    stage_store(stage_load(cur), 0);
-    __syncthreads();
-    for (int tt = 0; tt < n_kt; ++tt) {
-        const int buf = tt & 1;
-        const bool more = tt + 1 < n_kt;
-        const TileSR nxt = to_sr(nraw);
-        nraw = desc(tt + 2);
-        decltype(stage_load(nxt)) st;
-        if (more)
-            st = stage_load(nxt);
+    auto run = [&](TileSR kt, int buf) {
         if constexpr (R > 0) {
-            const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
+            const bool need_mask = (kt.n_valid < kKeyTile) || (kt.key0 + kt.n_valid - 1 > wave_min_pos);
             if (need_mask)
-                tile_exact(cur, buf, std::true_type{});
+                tile_exact(kt, buf, std::true_type{});
             else if (!tile_ref(buf))
-                tile_exact(cur, buf, std::false_type{});
+                tile_exact(kt, buf, std::false_type{});
         }
-        if (more)
-            stage_store(st, buf ^ 1);
+    };
+    TileSR c0 = to_sr(desc(0)), c1 = to_sr(desc(1));
+    stage_store(stage_load(c0), 0);
+    if (n_kt > 1)
+        stage_store(stage_load(c1), 1);
+    uint32_t raw0 = desc(2), raw1 = desc(3);
+    __syncthreads();
+    const int n_steps = (n_kt + 1) / 2;
+    for (int g = 0; g < n_steps; ++g) {
+        const int base = (g & 1) * 2;
+        const int ta = 2 * g + 2, tb = 2 * g + 3;   // tiles loaded during this step
+        const TileSR s0 = to_sr(raw0), s1 = to_sr(raw1);
+        raw0 = desc(ta + 2);
+        raw1 = desc(tb + 2);
+        decltype(stage_load(s0)) sa, sb;
+        if (ta < n_kt)
+            sa = stage_load(s0);
+        if (tb < n_kt)
+            sb = stage_load(s1);
+        run(c0, base);
+        if (2 * g + 1 < n_kt)
+            run(c1, base + 1);
+        if (ta < n_kt)
+            stage_store(sa, base ^ 2);
+        if (tb < n_kt)
+            stage_store(sb, (base ^ 2) + 1);
         __syncthreads();
-        cur = nxt;
+        c0 = s0;
+        c1 = s1;
     }
 
     // The four lane groups of a row hold partial (max, sum) states: combine
@@ -206,8 +223,8 @@ __global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnA
     constexpr int TILE = kKeyTile * 2 * D;
     constexpr int NT = kLseWaves * 64;
     using Stg = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[4][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 4 : 1][KV8 ? TILE : 16];
 
     const ItemDesc it = a.items[blockIdx.x];
     if (it.n_rowtiles == 0 || it.n_ktiles == 0)
