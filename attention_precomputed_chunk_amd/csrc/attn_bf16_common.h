@@ -133,6 +133,26 @@ struct Stager {
             if (chunk[i] >= 0)
                 *reinterpret_cast<u32x4 *>((is_v(i) ? lv : lk) + lds[i]) = st.c[i];
     }
+
+    // A K-only stager moving the same chunks of the tile's V instead (into
+    // V's swizzled slots).
+    __device__ __forceinline__ S load_v(TileSR kt, int kv_head) const
+    {
+        static_assert(!WITH_V, "K-only stager");
+        TileSR v = kt;
+        v.K = kt.V;
+        return load(v, kv_head);
+    }
+    __device__ __forceinline__ void store_v(const S st, unsigned char *lv) const
+    {
+        static_assert(!WITH_V, "K-only stager");
+#pragma unroll
+        for (int i = 0; i < S::PER; ++i)
+            if (chunk[i] >= 0) {
+                const int key = chunk[i] / NCH, ch = chunk[i] % NCH;
+                *reinterpret_cast<u32x4 *>(lv + key * ROW + ((ch ^ vswz<NCH>(key)) << 4)) = st.c[i];
+            }
+    }
 };
 
 // Eight codes (two dwords, lowest byte first) times float32 scales.

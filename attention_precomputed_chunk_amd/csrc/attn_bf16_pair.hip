@@ -188,10 +188,17 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     // the producers load tile s + 1 from global memory and store it into
     // lds_k[(s + 1) & 1], lds_v[(s + 1) % 3]. Every read of a buffer ends
     // before the barrier after which it is refilled.
-    constexpr int NTP = kWaves * 64;   // the producers stage the tiles of sweep 2
-    const Stager<NCH, true, NTP> stg2(tid & (NTP - 1));
-    if (wave < kWaves)
-        stg2.store(stg2.load(to_sr(desc(0)), it.kv_head), lds_k[0], lds_v[0]);
+    // The producers stage K and the consumers V (the producers' scores,
+    // exponentials and impact sums are the critical path).
+    constexpr int NTP = kWaves * 64;
+    const Stager<NCH, false, NTP> stgk(tid & (NTP - 1));   // K of a tile over one role's threads
+    {
+        const TileSR t = to_sr(desc(0));
+        if (wave < kWaves)
+            stgk.store(stgk.load(t, it.kv_head), lds_k[0], nullptr);
+        else
+            stgk.store_v(stgk.load_v(t, it.kv_head), lds_v[0]);
+    }
     __syncthreads();   // also publishes lds_lse
 
     const int pair = wave & (kWaves - 1);
@@ -267,9 +274,9 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
         for (int s = 0; s <= n_kt; ++s) {
             const TileSR nxt = to_sr(craw);
             craw = desc(s + 2);
-            Staged<NCH, true, NTP> st;
+            Staged<NCH, false, NTP> st;
             if (s + 1 < n_kt)
-                st = stg2.load(nxt, it.kv_head);
+                st = stgk.load(nxt, it.kv_head);
             if (s < n_kt) {
                 if ((cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos))
                     tile(cur, s & 1, std::true_type{});
@@ -277,10 +284,9 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
                     tile(cur, s & 1, std::false_type{});
             }
             if (s + 1 < n_kt)
-                stg2.store(st, lds_k[(s + 1) & 1], lds_v[vb]);
+                stgk.store(st, lds_k[(s + 1) & 1], nullptr);
             __syncthreads();
             cur = nxt;
-            vb = vb == 2 ? 0 : vb + 1;
         }
     } else {
         // ------------------------------------------------------------ consumer
@@ -297,6 +303,9 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
         for (int s = 0; s <= n_kt; ++s) {
             const TileSR nxt = to_sr(nraw);
             nraw = desc(s + 2);
+            Staged<NCH, false, NTP> st;
+            if (s + 1 < n_kt)
+                st = stgk.load_v(nxt, it.kv_head);
             if (s > 0) {
                 const int pbuf = (s - 1) & 1;
                 const int vprev = vb == 2 ? 0 : vb + 1;
@@ -322,6 +331,8 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
                         o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt], o[rt][dt], 0, 0, 0);
                 }
             }
+            if (s + 1 < n_kt)
+                stgk.store_v(st, lds_v[vb]);
             __syncthreads();
             prev = cur;
             cur = nxt;

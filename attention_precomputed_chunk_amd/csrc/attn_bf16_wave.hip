@@ -40,35 +40,46 @@
 
 namespace crkv {
 
-template <int D, int RT, bool CROSS, bool KV8, bool LSE_IN>
-__global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnArgs a)
+// Who moves the key tiles into LDS and writes the impact partials: every
+// wave its share (kSideShare), or, when the block's last wave holds at least
+// kSideSlack fewer row tiles than the others, that wave alone (kSideAll)
+// while the others only compute (kSideNone). The side work then runs in the
+// last wave's slack instead of on every wave's critical path.
+enum { kSideShare = 0, kSideNone = 1, kSideAll = 2 };
+constexpr int kSideSlack = 2;
+
+// One wave's part of a work item: RT row tiles per wave in the block (the
+// stride of the waves' tile runs), RTW of them this wave's (RTW <= RT; the
+// last wave of a partial block holds fewer).
+template <int D, int RT, int RTW, int SIDE, bool CROSS, bool KV8, bool LSE_IN>
+__device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
+                                          unsigned char (*lds_k)[kKeyTile * 2 * D],
+                                          unsigned char (*lds_v)[kKeyTile * 2 * D],
+                                          unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16],
+                                          float (*lds_imp)[kWaves][kKeyTile])
 {
+    static_assert(SIDE == kSideShare || (LSE_IN && !KV8), "side-work split: bf16, pass 1 on its own");
+    static_assert(RTW >= 0 && RTW <= RT && (RTW > 0 || SIDE == kSideAll), "row tiles of the wave");
+    constexpr int RTA = RTW > 0 ? RTW : 1;     // array extents
     constexpr int NT = kThreads;
     constexpr int NW = kWaves;
     constexpr int KS = D / 32;                 // MFMA k-steps along d
     constexpr int DT = D / 16;                 // output d tiles
     constexpr int NCH = D / 8;                 // 16-byte chunks per row
     constexpr int ROW = 2 * D;                 // LDS bytes per K or V row
-    constexpr int TILE = kKeyTile * ROW;       // LDS bytes per K (or V) tile
     static_assert(kKeyTile == 32, "tile geometry");
     // bf16 segments are staged as they are; 8-bit ones are widened on the way
     // (K into a bf16 hi/lo pair of tiles, V into one bf16 tile)
     using Stg1 = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
-    using Stg2 = std::conditional_t<KV8, StagerQ8<D, true, NT>, Stager<NCH, true, NT>>;
+    using Stg2 = std::conditional_t<KV8, StagerQ8<D, true, NT>,
+                                    std::conditional_t<SIDE == kSideAll, Stager<NCH, true, 64>, Stager<NCH, true, NT>>>;
+    constexpr bool STAGES = SIDE != kSideNone;   // this wave moves key tiles
     const Stg1 stg1(threadIdx.x);
-    const Stg2 stg2(threadIdx.x);
-
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];   // K lo (8-bit)
-    __shared__ float lds_imp[2][NW][kKeyTile];
+    const Stg2 stg2(SIDE == kSideAll ? (int)(threadIdx.x & 63) : (int)threadIdx.x);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const ItemDesc it = a.items[blockIdx.x];
-    if (it.n_rowtiles == 0)
-        return;
     const ProbDesc pr = a.probs[it.prob];
     const int G = a.G;
     const float c = a.c_log2;
@@ -88,10 +99,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             stg.store(st, lds_k[buf], lds_v[buf]);
     };
 
-    int row_pos[RT];
-    bf16x8 qf[RT][KS];
+    int row_pos[RTA];
+    bf16x8 qf[RTA][KS];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
         const int r = (t0 + rt) * kRowTile + li;
         const bool valid = r < packed_total;
         const int j = r / G;
@@ -118,9 +129,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     const int n_kt = it.n_ktiles;   // key tiles kt0 .. kt0 + n_kt - 1 of the problem's list
     const int kt0 = it.kt_begin;
     // ---------------------------------------------------------------- sweep 1: row lse
-    float row_m[RT], row_l[RT];
+    float row_m[RTA], row_l[RTA];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
         row_m[rt] = -INFINITY;
         row_l[rt] = 0.f;
     }
@@ -136,7 +147,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                     kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
             }
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RTW; ++rt) {
             f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -182,10 +193,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                 if constexpr (KV8)
                     kfl[sub][ks] = *reinterpret_cast<const bf16x8 *>(&lds_kl[buf][k_off(sub, ks)]);
             }
-        float sum[RT];
+        float sum[RTA];
         bool big = false;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RTW; ++rt) {
             f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -209,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         if (__builtin_amdgcn_ballot_w64(big))
             return false;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RTW; ++rt)
             row_l[rt] += sum[rt];
         return true;
     };
@@ -246,9 +257,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     // padded rows get +inf so every weight they would produce is 0. With
     // LSE_IN pass 1 ran as attn_lse_kernel, one state per range of the block
     // (written for the block's real row tiles only).
-    float lse2[RT];
+    float lse2[RTA];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
         if constexpr (LSE_IN) {
             lse2[rt] = (row_pos[rt] < 0x3fffffff) ? merged_lse(a, it, (wave * RT + rt) * kRowTile + li, c) : INFINITY;
         } else {
@@ -260,16 +271,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     }
 
     // ---------------------------------------------------------------- sweep 2: P.V and impact
-    f32x4 o[RT][DT];
+    f32x4 o[RTA][DT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
             o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const gptr<float> partial = as_global(pr.partial) + (size_t)it.slot * pr.n_keys;
     auto flush_impact = [&](int tt, TileSR kt, int buf) {
-        if (wave == tt % NW) {
+        const bool mine = SIDE == kSideAll || (SIDE == kSideShare && wave == tt % NW);
+        if (mine) {
             if (lane < kt.n_valid) {
                 float sum = lds_imp[buf][0][lane];
 #pragma unroll
@@ -302,7 +314,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         }
         float imp[8];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RTW; ++rt) {
             f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -395,9 +407,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 pprev;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RTW; ++rt) {
             f32x4 n0 = f32x4{0.f, 0.f, 0.f, 0.f}, n1 = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (rt + 1 < RT) {
+            if (rt + 1 < RTW) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf[rt + 1][ks], n0, 0, 0, 0);
@@ -434,7 +446,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
                 pprev[i] = (__bf16)p[i];
             constexpr int QK = (KV8 ? 4 : 2) * KS;   // score MFMAs of a row tile
             constexpr int n_mfma_max = QK + DT;
-            const int n_mfma = (rt + 1 < RT ? QK : 0) + (rt > 0 ? DT : 0);
+            const int n_mfma = (rt + 1 < RTW ? QK : 0) + (rt > 0 ? DT : 0);
 #pragma unroll
             for (int i = 0; i < n_mfma_max; ++i) {
                 if (i < n_mfma) {
@@ -448,7 +460,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-            o[RT - 1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev, o[RT - 1][dt], 0, 0, 0);
+            o[RTA - 1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev, o[RTA - 1][dt], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             imp[i] = row16_sum(imp[i]);
@@ -462,7 +474,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
     if (n_kt > 0) {
         TileSR cur = to_sr(desc(0)), prev = cur;
         uint32_t nraw = desc(1);
-        stage_store(stg2, stage_load(stg2, cur), 0);
+        if constexpr (STAGES)
+            stage_store(stg2, stage_load(stg2, cur), 0);
         __syncthreads();
         for (int tt = 0; tt < n_kt; ++tt) {
             const int buf = tt & 1;
@@ -470,16 +483,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             const TileSR nxt = to_sr(nraw);
             nraw = desc(tt + 2);
             decltype(stage_load(stg2, nxt)) st;
-            if (more)
+            if (STAGES && more)
                 st = stage_load(stg2, nxt);
             if (tt > 0)
                 flush_impact(tt - 1, prev, buf ^ 1);
-            const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
-            if (need_mask)
-                sweep2_tile(cur, buf, std::true_type{});
-            else
-                sweep2_tile_pipe(cur, buf);
-            if (more)
+            if constexpr (RTW > 0) {
+                const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
+                if (need_mask)
+                    sweep2_tile(cur, buf, std::true_type{});
+                else
+                    sweep2_tile_pipe(cur, buf);
+            } else {
+                // no rows: this wave's impact sums of the tile are zero
+                if ((lane & 15) == 0)
+                    for (int i = 0; i < 8; ++i)
+                        lds_imp[buf][wave][8 * (lane >> 4) + i] = 0.f;
+            }
+            if (STAGES && more)
                 stage_store(stg2, st, buf ^ 1);
             __syncthreads();
             prev = cur;
@@ -495,7 +515,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         const gptr<f32x4> part = as_global(reinterpret_cast<f32x4 *>(a.opart + it.opart)) +
                                  (size_t)it.range * (a.cap_rows * D / 4);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RTW; ++rt) {
             const int local = (wave * RT + rt) * kRowTile + li;
             if ((t0 + rt) * kRowTile + li >= packed_total)
                 continue;
@@ -506,7 +526,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
         return;
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
         const int r = (t0 + rt) * kRowTile + li;
         if (r >= packed_total)
             continue;
@@ -524,6 +544,42 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnA
             *reinterpret_cast<gptr<u32x2>>(orow + 16 * dt + 4 * lg) = u32x2{lo, hi};
         }
     }
+}
+
+
+template <int D, int RT, bool CROSS, bool KV8, bool LSE_IN>
+__global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnArgs a)
+{
+    constexpr int TILE = kKeyTile * 2 * D;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];   // K lo (8-bit)
+    __shared__ float lds_imp[2][kWaves][kKeyTile];
+    const ItemDesc it = a.items[blockIdx.x];
+    if (it.n_rowtiles == 0)
+        return;
+    if constexpr (LSE_IN && !KV8 && RT == 7) {
+        // the last wave's row tiles; with kSideSlack or more fewer than RT it
+        // takes over every wave's staging and impact flushes
+        const int last = it.n_rowtiles - (kWaves - 1) * RT;
+        if (last >= 0 && last <= RT - kSideSlack) {
+            const int wave = threadIdx.x >> 6;
+            if (wave < kWaves - 1) {
+                wave_body<D, RT, RT, kSideNone, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp);
+                return;
+            }
+            switch (last) {
+            case 0: wave_body<D, RT, 0, kSideAll, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp); break;
+            case 1: wave_body<D, RT, 1, kSideAll, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp); break;
+            case 2: wave_body<D, RT, 2, kSideAll, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp); break;
+            case 3: wave_body<D, RT, 3, kSideAll, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp); break;
+            case 4: wave_body<D, RT, 4, kSideAll, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp); break;
+            default: wave_body<D, RT, 5, kSideAll, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp); break;
+            }
+            return;
+        }
+    }
+    wave_body<D, RT, RT, kSideShare, CROSS, KV8, LSE_IN>(a, it, lds_k, lds_v, lds_kl, lds_imp);
 }
 
 template <int D, int RT, bool KV8, bool LSE_IN>
