@@ -270,7 +270,6 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
         };
         TileSR cur = to_sr(desc(0));
         uint32_t craw = desc(1);
-        int vb = 1;   // lds_v slot of tile s + 1
         for (int s = 0; s <= n_kt; ++s) {
             const TileSR nxt = to_sr(craw);
             craw = desc(s + 2);

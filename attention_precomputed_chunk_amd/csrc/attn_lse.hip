@@ -30,10 +30,13 @@
 
 namespace crkv {
 
-template <int D, int R, bool KV8, typename Stg>
+// SPLIT: only the waves with srank >= 0 move key tiles (the others only
+// score); otherwise every thread moves its share (srank unused).
+template <int D, int R, bool KV8, bool SPLIT, typename Stg>
 __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr, const Stg &stg,
                                          unsigned char (*lds_k)[kKeyTile * 2 * D],
-                                         unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int wave, int lane)
+                                         unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int wave, int lane,
+                                         int srank)
 {
     constexpr int KS = D / 32;
     constexpr int NCH = D / 8;
@@ -171,10 +174,13 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
                 tile_exact(kt, buf, std::false_type{});
         }
     };
+    const bool stages = !SPLIT || srank >= 0;   // wave-uniform
     TileSR c0 = to_sr(desc(0)), c1 = to_sr(desc(1));
-    stage_store(stage_load(c0), 0);
-    if (n_kt > 1)
-        stage_store(stage_load(c1), 1);
+    if (stages) {
+        stage_store(stage_load(c0), 0);
+        if (n_kt > 1)
+            stage_store(stage_load(c1), 1);
+    }
     uint32_t raw0 = desc(2), raw1 = desc(3);
     __syncthreads();
     const int n_steps = (n_kt + 1) / 2;
@@ -185,16 +191,16 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
         raw0 = desc(ta + 2);
         raw1 = desc(tb + 2);
         decltype(stage_load(s0)) sa, sb;
-        if (ta < n_kt)
+        if (stages && ta < n_kt)
             sa = stage_load(s0);
-        if (tb < n_kt)
+        if (stages && tb < n_kt)
             sb = stage_load(s1);
         run(c0, base);
         if (2 * g + 1 < n_kt)
             run(c1, base + 1);
-        if (ta < n_kt)
+        if (stages && ta < n_kt)
             stage_store(sa, base ^ 2);
-        if (tb < n_kt)
+        if (stages && tb < n_kt)
             stage_store(sb, (base ^ 2) + 1);
         __syncthreads();
         c0 = s0;
@@ -216,13 +222,35 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
     }
 }
 
+// Row tiles beyond a multiple of 8 (r = n % 8 < 4) go one each to waves
+// 0 .. r - 1, so SIMDs 0 .. r - 1 hold one row tile more than the others.
+// Then (bf16) two waves of the lighter SIMDs move every key tile and the
+// busier SIMDs only score.
+template <int D, bool KV8, bool SPLIT>
+__device__ __forceinline__ void lse_dispatch(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr,
+                                             unsigned char (*lds_k)[kKeyTile * 2 * D],
+                                             unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int wave,
+                                             int lane, int srank)
+{
+    constexpr int NCH = D / 8;
+    constexpr int NT = SPLIT ? 128 : kLseWaves * 64;   // threads that move key tiles
+    using Stg = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
+    const Stg stg(SPLIT ? (srank < 0 ? 0 : srank) : (int)threadIdx.x);
+    // this wave's row tiles: wave, wave + 8, ... below n_rowtiles
+    const int mine = wave < it.n_rowtiles ? (it.n_rowtiles - wave + kLseWaves - 1) / kLseWaves : 0;
+    switch (mine) {
+    case 0: lse_body<D, 0, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
+    case 1: lse_body<D, 1, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
+    case 2: lse_body<D, 2, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
+    case 3: lse_body<D, 3, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
+    default: lse_body<D, 4, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
+    }
+}
+
 template <int D, bool KV8>
 __global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnArgs a)
 {
-    constexpr int NCH = D / 8;
     constexpr int TILE = kKeyTile * 2 * D;
-    constexpr int NT = kLseWaves * 64;
-    using Stg = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
     __shared__ __attribute__((aligned(16))) unsigned char lds_k[4][TILE];
     __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 4 : 1][KV8 ? TILE : 16];
 
@@ -232,16 +260,19 @@ __global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnA
     const ProbDesc pr = a.probs[it.prob];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const Stg stg(threadIdx.x);
-    // this wave's row tiles: wave, wave + 8, ... below n_rowtiles
-    const int mine = wave < it.n_rowtiles ? (it.n_rowtiles - wave + kLseWaves - 1) / kLseWaves : 0;
-    switch (mine) {
-    case 0: lse_body<D, 0, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
-    case 1: lse_body<D, 1, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
-    case 2: lse_body<D, 2, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
-    case 3: lse_body<D, 3, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
-    default: lse_body<D, 4, KV8>(a, it, pr, stg, lds_k, lds_kl, wave, lane); break;
+    static_assert(kLseWaves == 8 && kLseMaxRowTilesPerWave == 4, "a body per row-tile count");
+    if constexpr (!KV8) {
+        const int r = it.n_rowtiles % kLseWaves;
+        if (r >= 1 && r <= 3) {
+            // staging waves: the second waves of SIMDs 2 and 3 (r <= 2), or
+            // both waves of SIMD 3 (r = 3)
+            const int w0 = r <= 2 ? 6 : 3;
+            const int srank = wave == w0 ? lane : wave == 7 ? 64 + lane : -1;
+            lse_dispatch<D, KV8, true>(a, it, pr, lds_k, lds_kl, wave, lane, srank);
+            return;
+        }
     }
+    lse_dispatch<D, KV8, false>(a, it, pr, lds_k, lds_kl, wave, lane, -1);
 }
 
 // The items of a plan whose blocks hold at most kLseWaves *
