@@ -14,9 +14,9 @@
 // wave on the SIMD supplies the overlap. Pass 2 needs the output accumulators
 // of all its rows and so fills a SIMD's registers with one wave, but pass 1
 // needs only Q and two numbers per row: here 8 waves (two per SIMD) share
-// each staged K tile, and an item's row tiles are dealt to them round robin
-// (wave w takes tiles w, w + 8, ...). Each wave runs a body compiled for its
-// own number of row tiles (0 .. 4), so no padded tile is computed; every body
+// each staged K tile, and each wave takes a run of consecutive row tiles of
+// the item's block (lse_rows). Each wave runs a body compiled for its own
+// number of row tiles (0 .. 4), so no padded tile is computed; every body
 // meets the same barriers.
 //
 // The arithmetic per key tile is the one-wave kernel's pass 1: scores on the
@@ -32,10 +32,11 @@ namespace crkv {
 
 // SPLIT: only the waves with srank >= 0 move key tiles (the others only
 // score); otherwise every thread moves its share (srank unused).
+// The wave's row tiles are first .. first + R - 1 of the block.
 template <int D, int R, bool KV8, bool SPLIT, typename Stg>
 __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr, const Stg &stg,
                                          unsigned char (*lds_k)[kKeyTile * 2 * D],
-                                         unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int wave, int lane,
+                                         unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int first, int lane,
                                          int srank)
 {
     constexpr int KS = D / 32;
@@ -53,11 +54,11 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
     float row_m[RR], row_l[RR];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        load_q_rows<KS>(pr, it, G, it.tile_begin + wave + i * kLseWaves, li, lg, qf[i], row_pos[i]);
+        load_q_rows<KS>(pr, it, G, it.tile_begin + first + i, li, lg, qf[i], row_pos[i]);
         row_m[i] = -INFINITY;
         row_l[i] = 0.f;
     }
-    const int wave_min_pos = pr.pos0 + ((it.tile_begin + wave) * kRowTile) / G;
+    const int wave_min_pos = pr.pos0 + ((it.tile_begin + first) * kRowTile) / G;
 
     const int kkey0 = 8 * (li >> 2) + (li & 3);
     const int ksw = kswz<NCH>(kkey0);
@@ -216,16 +217,30 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
         float m = row_m[i], l = row_l[i];
         merge_state(m, l, __shfl_xor(m, 16), __shfl_xor(l, 16), c);
         merge_state(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32), c);
-        const int local = (wave + i * kLseWaves) * kRowTile + li;   // packed row inside the item's block
+        const int local = (first + i) * kRowTile + li;   // packed row inside the item's block
         if (lg == 0)
             state[local] = f32x2{m, l};
     }
 }
 
-// Row tiles beyond a multiple of 8 (r = n % 8 < 4) go one each to waves
-// 0 .. r - 1, so SIMDs 0 .. r - 1 hold one row tile more than the others.
-// Then (bf16) two waves of the lighter SIMDs move every key tile and the
-// busier SIMDs only score.
+// Row tiles per wave. SIMD s (waves s and s + 4) takes n / 4 row tiles of
+// the block's n, one more for s < n % 4. Of a SIMD's two waves the first
+// keeps issue priority and, with equal shares, finishes its step while the
+// second has done about half of its own and then runs alone at a lone
+// wave's rate; the first wave therefore takes about two thirds of the
+// SIMD's row tiles (at most 4), so that both run until the barrier. Waves
+// hold consecutive row tiles, in wave order.
+__device__ __forceinline__ int lse_rows(int n, int wave)
+{
+    const int s = wave & 3;
+    const int sc = n / 4 + (s < n % 4 ? 1 : 0);
+    const int first = min(kLseMaxRowTilesPerWave, (2 * sc + 1) / 3);
+    return wave < 4 ? first : sc - first;
+}
+
+// With n % 4 in 1 .. 3, SIMDs 0 .. n % 4 - 1 hold one row tile more than the
+// others; then (bf16) two waves of the lighter SIMDs move every key tile and
+// the busier SIMDs only score.
 template <int D, bool KV8, bool SPLIT>
 __device__ __forceinline__ void lse_dispatch(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr,
                                              unsigned char (*lds_k)[kKeyTile * 2 * D],
@@ -236,14 +251,16 @@ __device__ __forceinline__ void lse_dispatch(const AttnArgs &a, const ItemDesc &
     constexpr int NT = SPLIT ? 128 : kLseWaves * 64;   // threads that move key tiles
     using Stg = std::conditional_t<KV8, StagerQ8<D, false, NT>, Stager<NCH, false, NT>>;
     const Stg stg(SPLIT ? (srank < 0 ? 0 : srank) : (int)threadIdx.x);
-    // this wave's row tiles: wave, wave + 8, ... below n_rowtiles
-    const int mine = wave < it.n_rowtiles ? (it.n_rowtiles - wave + kLseWaves - 1) / kLseWaves : 0;
-    switch (mine) {
-    case 0: lse_body<D, 0, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
-    case 1: lse_body<D, 1, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
-    case 2: lse_body<D, 2, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
-    case 3: lse_body<D, 3, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
-    default: lse_body<D, 4, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, wave, lane, srank); break;
+    const int n = it.n_rowtiles;
+    int first = 0;
+    for (int w = 0; w < wave; ++w)
+        first += lse_rows(n, w);
+    switch (lse_rows(n, wave)) {
+    case 0: lse_body<D, 0, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, first, lane, srank); break;
+    case 1: lse_body<D, 1, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, first, lane, srank); break;
+    case 2: lse_body<D, 2, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, first, lane, srank); break;
+    case 3: lse_body<D, 3, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, first, lane, srank); break;
+    default: lse_body<D, 4, KV8, SPLIT>(a, it, pr, stg, lds_k, lds_kl, first, lane, srank); break;
     }
 }
 
@@ -262,8 +279,8 @@ __global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnA
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     static_assert(kLseWaves == 8 && kLseMaxRowTilesPerWave == 4, "a body per row-tile count");
     if constexpr (!KV8) {
-        const int r = it.n_rowtiles % kLseWaves;
-        if (r >= 1 && r <= 3) {
+        const int r = it.n_rowtiles % 4;
+        if (r >= 1) {
             // staging waves: the second waves of SIMDs 2 and 3 (r <= 2), or
             // both waves of SIMD 3 (r = 3)
             const int w0 = r <= 2 ? 6 : 3;

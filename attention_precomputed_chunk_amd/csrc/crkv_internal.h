@@ -127,7 +127,7 @@ struct CombineArgs {
 };
 
 // Pass 1 as its own kernel (attn_lse_kernel): kLseWaves waves per workgroup,
-// two per SIMD, the item's row tiles dealt to them round robin.
+// two per SIMD, each holding a run of the item's row tiles.
 constexpr int kLseWaves = 8;
 constexpr int kLseMaxRowTilesPerWave = 4;   // items of up to 32 row tiles
 constexpr int kCUs = 256;                   // MI355X compute units (the planner's makespan model)
