@@ -259,14 +259,10 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
                     pb[i] = (__bf16)p[i];
                 lds_p[buf][pair][rt][lane] = pb;
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                imp[i] = row16_sum(imp[i]);
-            if (li == 0) {
-                float *dst = &lds_imp[buf][pair][8 * lg];
-                *reinterpret_cast<float4 *>(dst) = make_float4(imp[0], imp[1], imp[2], imp[3]);
-                *reinterpret_cast<float4 *>(dst + 4) = make_float4(imp[4], imp[5], imp[6], imp[7]);
-            }
+            float i0, i1;
+            row16_sum8(imp, li, i0, i1);
+            if ((li & 3) == 0)
+                *reinterpret_cast<float2 *>(&lds_imp[buf][pair][8 * lg + 2 * (li >> 2)]) = make_float2(i0, i1);
         };
         TileSR cur = to_sr(desc(0));
         uint32_t craw = desc(1);

@@ -360,14 +360,10 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
             for (int dt = 0; dt < DT; ++dt)
                 o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, o[rt][dt], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            imp[i] = row16_sum(imp[i]);
-        if (li == 0) {
-            float *dst = &lds_imp[buf][wave][8 * lg];
-            *reinterpret_cast<float4 *>(dst) = make_float4(imp[0], imp[1], imp[2], imp[3]);
-            *reinterpret_cast<float4 *>(dst + 4) = make_float4(imp[4], imp[5], imp[6], imp[7]);
-        }
+        float i0, i1;
+        row16_sum8(imp, li, i0, i1);
+        if ((li & 3) == 0)
+            *reinterpret_cast<float2 *>(&lds_imp[buf][wave][8 * lg + 2 * (li >> 2)]) = make_float2(i0, i1);
     };
 
     // Unmasked tiles, software-pipelined over the row tiles: stage rt issues
@@ -461,14 +457,10 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
             o[RTA - 1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pprev, o[RTA - 1][dt], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            imp[i] = row16_sum(imp[i]);
-        if (li == 0) {
-            float *dst = &lds_imp[buf][wave][8 * lg];
-            *reinterpret_cast<float4 *>(dst) = make_float4(imp[0], imp[1], imp[2], imp[3]);
-            *reinterpret_cast<float4 *>(dst + 4) = make_float4(imp[4], imp[5], imp[6], imp[7]);
-        }
+        float i0, i1;
+        row16_sum8(imp, li, i0, i1);
+        if ((li & 3) == 0)
+            *reinterpret_cast<float2 *>(&lds_imp[buf][wave][8 * lg + 2 * (li >> 2)]) = make_float2(i0, i1);
     };
 
     if (n_kt > 0) {

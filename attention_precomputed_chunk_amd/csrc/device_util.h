@@ -47,6 +47,29 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
+// Sums of eight per-lane values v[0..7] over the 16 lanes of a DPP row,
+// transposed while they are summed: lane li of the row receives the totals
+// of values 2 (li / 4) (s0) and 2 (li / 4) + 1 (s1). Each of the first two
+// steps pairs lanes (li ^ 8, then the mirror image within each half of 8)
+// so that each lane keeps half of the values it holds; the last two sum
+// within quads. 22 vector instructions against 48 for eight row16_sum.
+__device__ __forceinline__ void row16_sum8(const float (&v)[8], int li, float &s0, float &s1)
+{
+    const bool lo8 = li < 8;
+    const bool lo4 = (li & 4) == 0;
+    float r1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)   // r1[k]: value k + 4 (li >= 8), over lanes li and li ^ 8
+        r1[k] = (lo8 ? v[k] : v[k + 4]) + dpp_mov<0x128>(lo8 ? v[k + 4] : v[k]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {   // value j + 2 ((li & 4) != 0) + 4 (li >= 8), over 4 lanes
+        float r = (lo4 ? r1[j] : r1[j + 2]) + dpp_mov<0x141>(lo4 ? r1[j + 2] : r1[j]);
+        r += dpp_mov<0x4E>(r);   // quad lanes ^ 2
+        r += dpp_mov<0xB1>(r);   // quad lanes ^ 1
+        (j == 0 ? s0 : s1) = r;
+    }
+}
+
 // Combine two (max, sum) softmax states; maxima are raw scores, the sums are
 // of exp2((s - max) * c).
 __device__ __forceinline__ void merge_state(float &m, float &l, float m2, float l2, float c)
