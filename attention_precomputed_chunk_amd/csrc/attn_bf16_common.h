@@ -22,7 +22,7 @@ constexpr int kWsThreads = 2 * kWaves * 64;   // pair kernel: a producer and a c
 // K tile slot of 16-byte chunk `ch` of row `key`: the 16 keys one A operand
 // reads (keys 8(i>>2) + 4s + (i&3)) land in 16 distinct slots.
 template <int NCH>
-__device__ __forceinline__ int kswz(int key)
+__host__ __device__ constexpr int kswz(int key)
 {
     return NCH == 16 ? ((key & 3) | (((key >> 3) & 3) << 2)) : ((key & 3) | (((key >> 3) & 1) << 2));
 }
@@ -30,7 +30,7 @@ __device__ __forceinline__ int kswz(int key)
 // rows one transposed read touches (4 consecutive keys, 8 for two lane
 // groups) get distinct 32-byte bank groups.
 template <int NCH>
-__device__ __forceinline__ int vswz(int key)
+__host__ __device__ constexpr int vswz(int key)
 {
     return NCH == 16 ? 2 * ((key & 3) | (((key >> 3) & 1) << 2)) : 2 * (key & 3);
 }
@@ -79,29 +79,67 @@ struct Staged {
     u32x4 c[PER];
 };
 
-// A thread's fixed part of the staging: which chunk it moves and where the
-// chunk lands in a tile buffer (the swizzled LDS byte offset), computed once.
+// A thread's fixed part of the staging, computed once. Thread t moves the
+// chunks t + i NT: with NT a multiple of NCH its column chunk ch = t % NCH is
+// the same for every i and its key advances by KS = NT / NCH rows per i. The
+// XOR swizzle of row k0 + i KS is then the swizzle of the thread's first
+// row k0 XOR a value that depends on i alone (kconst / vconst, checked at
+// compile time for every thread), so the LDS byte offset of chunk i is one
+// of at most four per-thread bases (K; two for V) plus the compile-time
+// i KS ROW, and the global byte offset is 16 t plus the compile-time
+// i NT 16: no per-chunk address arithmetic at run time beyond the
+// instructions' immediate offsets.
 // WITH_V stages K then V of one tile; otherwise K alone.
 template <int NCH, bool WITH_V, int NT>
 struct Stager {
     using S = Staged<NCH, WITH_V, NT>;
     static constexpr int ROW = NCH * 16;
+    static constexpr int KS = NT / NCH;
+    static_assert(NT % NCH == 0 && KS % 4 == 0, "a thread keeps its column chunk and its key's low two bits");
     static constexpr bool is_v(int i) { return WITH_V && i * NT >= S::CH; }
-    int chunk[S::PER];      // chunk index inside its K (or V) tile, -1 if none
-    uint32_t lds[S::PER];   // LDS byte offset inside a tile buffer
+    static constexpr int rel(int i) { return is_v(i) ? i - S::CH / NT : i; }   // chunk step inside K or V
+    static constexpr int kconst(int r) { return kswz<NCH>(r * KS) ^ kswz<NCH>(0); }
+    static constexpr int vconst(int r) { return vswz<NCH>(r * KS) ^ vswz<NCH>(0); }
+    static constexpr int kslot(int r) { return kconst(r) >> 2; }   // 0 .. 3
+    static constexpr int vslot(int r) { return vconst(r) >> 3; }   // 0 .. 1
+    static constexpr bool split_ok()
+    {
+        for (int t = 0; t < NT; ++t)
+            for (int r = 0; r * NT < S::CH; ++r) {
+                const int k0 = t / NCH;
+                if (kswz<NCH>(k0 + r * KS) != (kswz<NCH>(k0) ^ kconst(r)) ||
+                    vswz<NCH>(k0 + r * KS) != (vswz<NCH>(k0) ^ vconst(r)) || (kconst(r) & 3) != 0 ||
+                    kslot(r) > 3 || (vconst(r) & 7) != 0 || vslot(r) > 1)
+                    return false;
+            }
+        return true;
+    }
+    static_assert(split_ok(), "swizzle of a thread's rows = its first row's XOR a per-step constant");
+    static constexpr bool all_valid = S::TOTAL % NT == 0;
+
+    uint32_t goff;      // byte offset of the thread's first chunk in a K (or V) tile
+    uint32_t kb[4];     // LDS byte offsets of the thread's K chunks, per kslot
+    uint32_t vb[2];     // the same in a V tile, per vslot
+    bool last_ok;       // chunk PER - 1 exists (always, when all_valid)
+    int k0, ch;
 
     __device__ __forceinline__ explicit Stager(int t)
     {
+        k0 = t / NCH;
+        ch = t % NCH;
+        goff = (uint32_t)t * 16u;
+        const int uk = ch ^ kswz<NCH>(k0), uv = ch ^ vswz<NCH>(k0);
 #pragma unroll
-        for (int i = 0; i < S::PER; ++i) {
-            const int x = t + i * NT;
-            const int c = is_v(i) ? x - S::CH : x;
-            const int key = c / NCH, ch = c % NCH;
-            const int sw = is_v(i) ? vswz<NCH>(key) : kswz<NCH>(key);
-            chunk[i] = x < S::TOTAL ? c : -1;
-            lds[i] = (uint32_t)(key * ROW + ((ch ^ sw) << 4));
-        }
+        for (int q = 0; q < 4; ++q)
+            kb[q] = (uint32_t)(k0 * ROW + ((uk ^ (q << 2)) << 4));
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            vb[q] = (uint32_t)(k0 * ROW + ((uv ^ (q << 3)) << 4));
+        last_ok = all_valid || t + (S::PER - 1) * NT < S::TOTAL;
     }
+    __device__ __forceinline__ bool has(int i) const { return i < S::PER - 1 || last_ok; }
+    __device__ __forceinline__ uint32_t klds(int i) const { return kb[kslot(rel(i))] + (uint32_t)(rel(i) * KS * ROW); }
+    __device__ __forceinline__ uint32_t vlds(int i) const { return vb[vslot(rel(i))] + (uint32_t)(rel(i) * KS * ROW); }
 
     // Row `key` of KV head g of the tile's segment starts g * seg_len rows past
     // the tile's base; keys past n_valid repeat the last real key (masked later).
@@ -109,18 +147,21 @@ struct Stager {
     {
         S st;
         const size_t head = (size_t)kv_head * kt.seg_len * NCH;
-        const gptr<const u32x4> kb = kt.K + head, vb = kt.V + head;
+        const gptr<const unsigned char> kbase = reinterpret_cast<gptr<const unsigned char>>(kt.K + head);
+        const gptr<const unsigned char> vbase = reinterpret_cast<gptr<const unsigned char>>(kt.V + head);
         if (kt.n_valid == kKeyTile) {
 #pragma unroll
             for (int i = 0; i < S::PER; ++i)
-                if (chunk[i] >= 0)
-                    st.c[i] = is_v(i) ? vb[chunk[i]] : kb[chunk[i]];
+                if (has(i))
+                    st.c[i] = *reinterpret_cast<gptr<const u32x4>>((is_v(i) ? vbase : kbase) + goff +
+                                                                   (uint32_t)(rel(i) * NT * 16));
         } else {
 #pragma unroll
             for (int i = 0; i < S::PER; ++i)
-                if (chunk[i] >= 0) {
-                    const int c = min(chunk[i] / NCH, kt.n_valid - 1) * NCH + chunk[i] % NCH;
-                    st.c[i] = is_v(i) ? vb[c] : kb[c];
+                if (has(i)) {
+                    const int key = min(k0 + rel(i) * KS, kt.n_valid - 1);
+                    st.c[i] = *reinterpret_cast<gptr<const u32x4>>((is_v(i) ? vbase : kbase) +
+                                                                   (uint32_t)((key * NCH + ch) * 16));
                 }
         }
         return st;
@@ -130,8 +171,8 @@ struct Stager {
     {
 #pragma unroll
         for (int i = 0; i < S::PER; ++i)
-            if (chunk[i] >= 0)
-                *reinterpret_cast<u32x4 *>((is_v(i) ? lv : lk) + lds[i]) = st.c[i];
+            if (has(i))
+                *reinterpret_cast<u32x4 *>(is_v(i) ? lv + vlds(i) : lk + klds(i)) = st.c[i];
     }
 
     // A K-only stager moving the same chunks of the tile's V instead (into
@@ -148,10 +189,8 @@ struct Stager {
         static_assert(!WITH_V, "K-only stager");
 #pragma unroll
         for (int i = 0; i < S::PER; ++i)
-            if (chunk[i] >= 0) {
-                const int key = chunk[i] / NCH, ch = chunk[i] % NCH;
-                *reinterpret_cast<u32x4 *>(lv + key * ROW + ((ch ^ vswz<NCH>(key)) << 4)) = st.c[i];
-            }
+            if (has(i))
+                *reinterpret_cast<u32x4 *>(lv + vlds(i)) = st.c[i];
     }
 };
 
