@@ -279,16 +279,24 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
             o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const gptr<float> partial = as_global(pr.partial) + (size_t)it.slot * pr.n_keys;
-    auto flush_impact = [&](int tt, TileSR kt, int buf) {
-        const bool mine = SIDE == kSideAll || (SIDE == kSideShare && wave == tt % NW);
-        if (mine) {
-            if (lane < kt.n_valid) {
-                float sum = lds_imp[buf][0][lane];
+    // A tile's partial: its waves' sums are read from LDS at the top of the
+    // next iteration (flush_read) and added and written after that
+    // iteration's arithmetic (flush_write), so the LDS latency hides under it.
+    auto flush_mine = [&](int tt) { return SIDE == kSideAll || (SIDE == kSideShare && wave == tt % NW); };
+    auto flush_read = [&](int tt, int buf, float (&fv)[NW]) {
+        if (flush_mine(tt) && lane < kKeyTile) {
 #pragma unroll
-                for (int w = 1; w < NW; ++w)
-                    sum += lds_imp[buf][w][lane];
-                partial[kt.key0 + lane] = sum;
-            }
+            for (int w = 0; w < NW; ++w)
+                fv[w] = lds_imp[buf][w][lane];
+        }
+    };
+    auto flush_write = [&](int tt, TileSR kt, const float (&fv)[NW]) {
+        if (flush_mine(tt) && lane < kt.n_valid) {
+            float sum = fv[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w)
+                sum += fv[w];
+            partial[kt.key0 + lane] = sum;
         }
     };
     // Tiles that need the causal or ragged-tail mask.
@@ -477,8 +485,9 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
             decltype(stage_load(stg2, nxt)) st;
             if (STAGES && more)
                 st = stage_load(stg2, nxt);
+            float fv[NW];
             if (tt > 0)
-                flush_impact(tt - 1, prev, buf ^ 1);
+                flush_read(tt - 1, buf ^ 1, fv);
             if constexpr (RTW > 0) {
                 const bool need_mask = (cur.n_valid < kKeyTile) || (cur.key0 + cur.n_valid - 1 > wave_min_pos);
                 if (need_mask)
@@ -491,13 +500,17 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
                     for (int i = 0; i < 8; ++i)
                         lds_imp[buf][wave][8 * (lane >> 4) + i] = 0.f;
             }
+            if (tt > 0)
+                flush_write(tt - 1, prev, fv);
             if (STAGES && more)
                 stage_store(stg2, st, buf ^ 1);
             __syncthreads();
             prev = cur;
             cur = nxt;
         }
-        flush_impact(n_kt - 1, prev, (n_kt - 1) & 1);
+        float fv[NW];
+        flush_read(n_kt - 1, (n_kt - 1) & 1, fv);
+        flush_write(n_kt - 1, prev, fv);
     }
 
     // ---------------------------------------------------------------- epilogue: out rows
