@@ -42,9 +42,16 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int *wave_tot)
     if (lane == 63)
         wave_tot[wave] = x;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w)
-        before += wave_tot[w];
+    // lane w < 16 holds wave w's total; an exclusive scan of those over the
+    // lanes, read at lane `wave`, is the sum of the waves before this one
+    int t = lane < kTopkWaves ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kTopkWaves; off <<= 1) {
+        const int y = __shfl_up(t, off);
+        if (lane >= off)
+            t += y;
+    }
+    const int before = __shfl(t, wave) - wave_tot[wave];
     __syncthreads();
     return x + before;
 }
@@ -52,7 +59,7 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int *wave_tot)
 __device__ __forceinline__ void topk_body(const TopkDesc td)
 {
     __shared__ __attribute__((aligned(16))) uint32_t keys[kTopkLdsKeys];   // then the sort's second buffer
-    __shared__ uint32_t whist[kTopkWaves][256];
+    __shared__ __attribute__((aligned(16))) uint32_t whist[kTopkWaves][256];
     __shared__ __attribute__((aligned(16))) unsigned long long sel[kTopkMaxK];
     __shared__ int wave_tot[kTopkWaves];
     __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
@@ -64,14 +71,28 @@ __device__ __forceinline__ void topk_body(const TopkDesc td)
     const bool in_lds = n <= kTopkLdsKeys;
     auto key_at = [&](int i) -> uint32_t { return in_lds ? keys[i] : order_key(td.value[i]); };
 
-    // keys, and the common prefix of all of them
+    // keys, and the common prefix of all of them (eight loads in flight per
+    // thread)
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int i = tid; i < n; i += kTopkThreads) {
-        const uint32_t kk = order_key(td.value[i]);
-        if (in_lds)
-            keys[i] = kk;
-        mn = min(mn, kk);
-        mx = max(mx, kk);
+    constexpr int kLoadBatch = 8;
+    for (int i0 = tid; i0 < n; i0 += kLoadBatch * kTopkThreads) {
+        float v[kLoadBatch];
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; ++j) {
+            const int i = i0 + j * kTopkThreads;
+            v[j] = i < n ? td.value[i] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; ++j) {
+            const int i = i0 + j * kTopkThreads;
+            if (i < n) {
+                const uint32_t kk = order_key(v[j]);
+                if (in_lds)
+                    keys[i] = kk;
+                mn = min(mn, kk);
+                mx = max(mx, kk);
+            }
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -108,17 +129,20 @@ __device__ __forceinline__ void topk_body(const TopkDesc td)
         }
         __syncthreads();
         if (wave == 0) {
-            // lane l owns digits 255-4l .. 252-4l (scanning from the top)
-            int c[4], tot = 0;
+            // lane l owns digits 255-4l .. 252-4l (scanning from the top),
+            // four adjacent bins read as one 16-byte word per wave
+            int c[4] = {0, 0, 0, 0}, tot = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int dg = 255 - 4 * lane - q;
-                int h = 0;
-                for (int w = 0; w < kTopkWaves; ++w)
-                    h += (int)whist[w][dg];
-                c[q] = h;
-                tot += h;
+            for (int w = 0; w < kTopkWaves; ++w) {
+                const uint4 h4 = *reinterpret_cast<const uint4 *>(&whist[w][252 - 4 * lane]);
+                c[0] += (int)h4.w;   // digit 255 - 4 lane
+                c[1] += (int)h4.z;
+                c[2] += (int)h4.y;
+                c[3] += (int)h4.x;   // digit 252 - 4 lane
             }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                tot += c[q];
             int incl = tot;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
