@@ -177,24 +177,54 @@ __device__ __forceinline__ void topk_body(const TopkDesc td)
     // counting keys above T and keys equal to T; scans of both counts place
     // every winner and decide which ties are taken (the first `remaining` in
     // index order).
-    const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
+    // (Keys in LDS: chunks of a multiple of 4 keys, read 16 bytes at a time.)
+    const int chunk0 = (n + kTopkThreads - 1) / kTopkThreads;
+    const int chunk = in_lds ? (chunk0 + 3) & ~3 : chunk0;
     const int b = min(n, tid * chunk), e = min(n, b + chunk);
     int gt = 0, eq = 0;
-    for (int i = b; i < e; ++i) {
-        const uint32_t kk = key_at(i);
+    auto count = [&](uint32_t kk) {
         gt += kk > T ? 1 : 0;
         eq += kk == T ? 1 : 0;
+    };
+    if (in_lds) {
+        for (int i = b; i < e; i += 4) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(&keys[i]);
+            count(q.x);
+            if (i + 1 < e)
+                count(q.y);
+            if (i + 2 < e)
+                count(q.z);
+            if (i + 3 < e)
+                count(q.w);
+        }
+    } else {
+        for (int i = b; i < e; ++i)
+            count(key_at(i));
     }
     const int gt_before = block_inclusive_scan(gt, wave_tot) - gt;
     const int eq_before = block_inclusive_scan(eq, wave_tot) - eq;
     int taken = min(eq_before, remaining);   // ties taken before this thread's chunk
     int pos = gt_before + taken;
-    for (int i = b; i < e; ++i) {
-        const uint32_t kk = key_at(i);
+    auto place = [&](uint32_t kk, int i) {
         if (kk > T || (kk == T && taken < remaining)) {
             sel[pos++] = ((unsigned long long)kk << 32) | (unsigned int)i;
             taken += kk == T ? 1 : 0;
         }
+    };
+    if (in_lds) {
+        for (int i = b; i < e; i += 4) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(&keys[i]);
+            place(q.x, i);
+            if (i + 1 < e)
+                place(q.y, i + 1);
+            if (i + 2 < e)
+                place(q.z, i + 2);
+            if (i + 3 < e)
+                place(q.w, i + 3);
+        }
+    } else {
+        for (int i = b; i < e; ++i)
+            place(key_at(i), i);
     }
     __syncthreads();
 
