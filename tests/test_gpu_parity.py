@@ -176,6 +176,34 @@ def test_pair_separate_pass1(case, rt, monkeypatch):
     run_and_compare(wl, label="pair%d-sep-small%d" % (rt, case))
 
 
+@pytest.mark.parametrize("build", [("wave", 7), ("pair", 6)], ids=["wave7", "pair6"])
+def test_pass1_every_block_size(build, monkeypatch):
+    """Pass 1 on its own (and pass 2 reading it) on row blocks of every size
+    from 1 to 28 row tiles in one batched call: problem n has G q_len = 16 n -
+    12 packed rows (G = 4), so its block holds n row tiles, the last one
+    partly padded. This covers every split of a block's row tiles between
+    the two waves of a SIMD, every residue of n modulo 4 (which SIMDs stage
+    the key tiles), and, in the one-wave kernel, every count of the last
+    wave's row tiles."""
+    kernel, rt = build
+    monkeypatch.setenv("CRKV_BF16_KERNEL", kernel)
+    monkeypatch.setenv("CRKV_ROW_TILES", str(rt))
+    monkeypatch.setenv("CRKV_SWEEP1", "split")
+    monkeypatch.setenv("CRKV_KEY_SPLIT", "off")
+    H, H_kv, d = 8, 2, 128
+    wl = workloads.Workload(spec=None, H=H, H_kv=H_kv, d=d, dtype="bf16", mode="query", r=0.1)
+    for n in range(1, 29):
+        rng = np.random.default_rng(np.random.SeedSequence(7100, spawn_key=(n,)))
+        wl.problems.append(workloads.make_problem(rng, [45, 38], 4 * n - 3, H, H_kv, d, "bf16", "query"))
+        wl.problem_ids.append(n - 1)
+    dw = DeviceWorkload(wl)
+    st = crkv.crkv_plan_stats(dw.problems, wl.H, wl.H_kv, wl.d, mode=wl.mode)
+    assert st["kernel"] == "bf16_" + kernel and st["row_tiles"] == rt and st["pass1_separate"] == 1, st
+    assert st["split_blocks"] == 0, st
+    say("pass 1, block sizes 1..28,", kernel, rt)
+    run_and_compare(wl, label="blocksizes-%s%d" % (kernel, rt))
+
+
 def test_key_ranges_repeat_bit_identical(monkeypatch):
     """A split plan (the planner's own: one short-query MHA layer, whose 32
     row blocks are cut into ranges) gives the same bits on every call."""
