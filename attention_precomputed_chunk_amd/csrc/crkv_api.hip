@@ -79,8 +79,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // (an upload on the caller's stream itself was measured to leave a gap of
 // tens of microseconds between kernels: the hand-off to the copy engine and
 // back). A slot is reused only after the event recorded behind the work that
-// read it has completed, so a slot in use is never overwritten. The ring's
-// mutex is held from plan_acquire to plan_release.
+// read it has completed, so a slot in use is never overwritten. A slot also
+// keeps a host copy of the bytes it last uploaded: a call whose tables are
+// byte-for-byte the same (a repeated call on the same tensors) skips the
+// copy and the wait, the slot's device half already holding them. The
+// ring's mutex is held from plan_acquire to plan_release.
 struct PlanRing {
     static constexpr int kSlots = 4;
     struct Slot {
@@ -90,6 +93,7 @@ struct PlanRing {
         hipEvent_t copied = nullptr;
         hipEvent_t consumed = nullptr;
         bool pending = false;
+        std::vector<unsigned char> shadow;   // the bytes of the last upload into `dev`
     };
     std::mutex mu;
     hipStream_t copy = nullptr;
@@ -164,6 +168,7 @@ int plan_acquire(PlanLease &l, size_t bytes)
         s.host = nullptr;
         s.dev = nullptr;
         s.cap = 0;
+        s.shadow.clear();
         const size_t cap = align_up(std::max<size_t>(bytes, 65536), 65536);
         e = hipHostMalloc(reinterpret_cast<void **>(&s.host), cap, hipHostMallocDefault);
         if (e != hipSuccess) {
@@ -190,6 +195,13 @@ int plan_acquire(PlanLease &l, size_t bytes)
 int plan_commit(PlanLease &l, size_t bytes, hipStream_t stream)
 {
     PlanRing::Slot &s = *l.slot;
+    // The slot's last upload completed before the work that read it, which
+    // plan_acquire waited for; identical bytes need no copy.
+    if (s.shadow.size() == bytes && std::memcmp(s.shadow.data(), s.host, bytes) == 0) {
+        l.committed = true;
+        return CRKV_OK;
+    }
+    s.shadow.clear();
     hipError_t e = hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, l.ring->copy);
     if (e != hipSuccess)
         return hip_fail(e, "hipMemcpyAsync(plan)");
@@ -200,6 +212,7 @@ int plan_commit(PlanLease &l, size_t bytes, hipStream_t stream)
         (void)hipStreamSynchronize(l.ring->copy);
         return hip_fail(e, "plan copy ordering");
     }
+    s.shadow.assign(s.host, s.host + bytes);
     l.committed = true;
     return CRKV_OK;
 }
