@@ -185,11 +185,11 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     // Step s (0 <= s <= n_kt): the producers score key tile s from lds_k[s & 1]
     // and write its P^T to lds_p[s & 1]; the consumers run P.V of tile s - 1
     // from lds_p[(s - 1) & 1] and lds_v[(s - 1) % 3] and flush its impact;
-    // the producers load tile s + 1 from global memory and store it into
-    // lds_k[(s + 1) & 1], lds_v[(s + 1) % 3]. Every read of a buffer ends
+    // tile s + 1 is loaded from global memory and stored into
+    // lds_k[(s + 1) & 1] (by the producers) and lds_v[(s + 1) % 3] (by the
+    // consumers, which have slack: the producers' scores, exponentials and
+    // impact sums are the critical path). Every read of a buffer ends
     // before the barrier after which it is refilled.
-    // The producers stage K and the consumers V (the producers' scores,
-    // exponentials and impact sums are the critical path).
     constexpr int NTP = kWaves * 64;
     const Stager<NCH, false, NTP> stgk(tid & (NTP - 1));   // K of a tile over one role's threads
     {
