@@ -86,9 +86,9 @@ struct Staged {
 // row k0 XOR a value that depends on i alone (kconst / vconst, checked at
 // compile time for every thread), so the LDS byte offset of chunk i is one
 // of at most four per-thread bases (K; two for V) plus the compile-time
-// i KS ROW, and the global byte offset is 16 t plus the compile-time
-// i NT 16: no per-chunk address arithmetic at run time beyond the
-// instructions' immediate offsets.
+// i KS ROW: no per-chunk LDS address arithmetic beyond the instructions'
+// immediate offsets. The global side clamps the key to the tile's last
+// valid one (a min and a shift-or per chunk).
 // WITH_V stages K then V of one tile; otherwise K alone.
 template <int NCH, bool WITH_V, int NT>
 struct Stager {
@@ -117,7 +117,6 @@ struct Stager {
     static_assert(split_ok(), "swizzle of a thread's rows = its first row's XOR a per-step constant");
     static constexpr bool all_valid = S::TOTAL % NT == 0;
 
-    uint32_t goff;      // byte offset of the thread's first chunk in a K (or V) tile
     uint32_t kb[4];     // LDS byte offsets of the thread's K chunks, per kslot
     uint32_t vb[2];     // the same in a V tile, per vslot
     bool last_ok;       // chunk PER - 1 exists (always, when all_valid)
@@ -127,7 +126,6 @@ struct Stager {
     {
         k0 = t / NCH;
         ch = t % NCH;
-        goff = (uint32_t)t * 16u;
         const int uk = ch ^ kswz<NCH>(k0), uv = ch ^ vswz<NCH>(k0);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -142,28 +140,26 @@ struct Stager {
     __device__ __forceinline__ uint32_t vlds(int i) const { return vb[vslot(rel(i))] + (uint32_t)(rel(i) * KS * ROW); }
 
     // Row `key` of KV head g of the tile's segment starts g * seg_len rows past
-    // the tile's base; keys past n_valid repeat the last real key (masked later).
+    // the tile's base; keys past n_valid repeat the last real key (masked
+    // later). Full and partial tiles share this one address form: with a
+    // second form for full tiles in its own branch, the compiler's wait-count
+    // pass took that branch's loads as possibly in flight where the other form
+    // reuses their registers, and made every chunk load wait for all earlier
+    // loads (the next tiles' descriptors and the previous tile's chunks).
     __device__ __forceinline__ S load(TileSR kt, int kv_head) const
     {
         S st;
         const size_t head = (size_t)kv_head * kt.seg_len * NCH;
         const gptr<const unsigned char> kbase = reinterpret_cast<gptr<const unsigned char>>(kt.K + head);
         const gptr<const unsigned char> vbase = reinterpret_cast<gptr<const unsigned char>>(kt.V + head);
-        if (kt.n_valid == kKeyTile) {
+        const int last = kt.n_valid - 1;
 #pragma unroll
-            for (int i = 0; i < S::PER; ++i)
-                if (has(i))
-                    st.c[i] = *reinterpret_cast<gptr<const u32x4>>((is_v(i) ? vbase : kbase) + goff +
-                                                                   (uint32_t)(rel(i) * NT * 16));
-        } else {
-#pragma unroll
-            for (int i = 0; i < S::PER; ++i)
-                if (has(i)) {
-                    const int key = min(k0 + rel(i) * KS, kt.n_valid - 1);
-                    st.c[i] = *reinterpret_cast<gptr<const u32x4>>((is_v(i) ? vbase : kbase) +
-                                                                   (uint32_t)((key * NCH + ch) * 16));
-                }
-        }
+        for (int i = 0; i < S::PER; ++i)
+            if (has(i)) {
+                const int key = min(k0 + rel(i) * KS, last);
+                st.c[i] = *reinterpret_cast<gptr<const u32x4>>((is_v(i) ? vbase : kbase) +
+                                                               (uint32_t)((key * NCH + ch) * 16));
+            }
         return st;
     }
 
