@@ -3,15 +3,26 @@
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_bf16, 64 lanes; li = lane % 16,
 // lg = lane / 16). Scores are taken as S^T = K . Q^T: A = 16 keys x 32 d from
-// LDS, B = 32 d x 16 rows held in registers for the whole sweep. The
-// accumulator gives lane (li, lg) row li and four keys. The A rows of the two
-// 16-key subtiles of a 32-key tile are permuted so that lane (li, lg) ends up
-// holding keys 8lg .. 8lg+7, which rounded to bf16 are exactly the B operand of
-// O^T = V^T . P^T. The V^T operand comes from V stored row-major in LDS
+// LDS (subtile s of a 32-key tile: keys 16 s .. 16 s + 15, in order), B =
+// 32 d x 16 rows held in registers for the whole sweep. The accumulator gives
+// lane (li, lg) row li and keys 16 s + 4 lg + e (e < 4) of subtile s; a
+// lane's eight scores of a tile (s = 0, 1), rounded to bf16, are exactly its
+// B operand of O^T = V^T . P^T when k index 8 lg + 4 s + e stands for key
+// 16 s + 4 lg + e. The V^T operand comes from V stored row-major in LDS
 // through ds_read_b64_tr_b16: inside each 16-lane group, if lane j reads four
 // bf16 B[j][0..3], lane i receives B[4e + i/4][i % 4] (e = 0..3), so lane j
-// addresses V[key0 + j/4][d0 + 4(j%4)] and two such reads give lane i the
-// eight keys of column d0 + i.
+// of group lg addresses V[16 r + 4 lg + j/4][d0 + 4(j%4)] in read r = 0, 1,
+// and the two reads give lane i the keys of its k indices for column d0 + i.
+//
+// LDS tiles: K and V rows are 2D bytes padded to 2D + 32, an odd number of
+// 32-byte units (9 at d = 128, 5 at d = 64). The padding, not a swizzle,
+// spreads the rows over the banks, so each fragment read of a lane is one
+// per-lane base plus a compile-time offset. A K read (16 bytes of row
+// 16 s + li at column chunk 4 ks + lg: consecutive rows in the lanes of a
+// group), a transposed V read (8 bytes of row 16 r + 4 lg + li/4) and the
+// staging writes (whole rows) meet no bank conflict at this stride; in-bounds
+// probes on gfx950 measured conflicts on K reads with rows padded by 16, 48
+// or 64 bytes or unpadded, and on V reads padded by 16 or 64.
 #pragma once
 #include "device_util.h"
 
@@ -19,14 +30,8 @@ namespace crkv {
 
 constexpr int kWsThreads = 2 * kWaves * 64;   // pair kernel: a producer and a consumer wave per SIMD
 
-// K tile slot of 16-byte chunk `ch` of row `key`: the 16 keys one A operand
-// reads (keys 8(i>>2) + 4s + (i&3)) land in 16 distinct slots.
-template <int NCH>
-__host__ __device__ constexpr int kswz(int key)
-{
-    return NCH == 16 ? ((key & 3) | (((key >> 3) & 3) << 2)) : ((key & 3) | (((key >> 3) & 1) << 2));
-}
-// V tile: even XOR values keep each 32-byte pair of chunks together, and the
+// XOR swizzle of the decode kernels' V tiles (16-byte chunk index of row
+// `key`): even values keep each 32-byte pair of chunks together, and the
 // rows one transposed read touches (4 consecutive keys, 8 for two lane
 // groups) get distinct 32-byte bank groups.
 template <int NCH>
@@ -34,6 +39,35 @@ __host__ __device__ constexpr int vswz(int key)
 {
     return NCH == 16 ? 2 * ((key & 3) | (((key >> 3) & 1) << 2)) : 2 * (key & 3);
 }
+
+// LDS row strides and tile sizes of the attention kernels (NCH = D / 8
+// 16-byte chunks of data per row).
+template <int NCH>
+constexpr int kRowK = NCH * 16 + 32;
+template <int NCH>
+constexpr int kRowV = NCH * 16 + 32;
+template <int NCH>
+constexpr int kTileK = kKeyTile * kRowK<NCH>;
+template <int NCH>
+constexpr int kTileV = kKeyTile * kRowV<NCH>;
+
+// Lane (li, lg)'s LDS byte offsets inside a tile: its K fragment of subtile
+// `sub` and k step `ks`, and its transposed V read `r` of d block dt.
+template <int NCH>
+__device__ __forceinline__ int k_frag_off(int li, int lg, int sub, int ks)
+{
+    return (16 * sub + li) * kRowK<NCH> + (4 * ks + lg) * 16;
+}
+template <int NCH>
+__device__ __forceinline__ int v_frag_off(int li, int lg, int r, int dt)
+{
+    return (16 * r + 4 * lg + (li >> 2)) * kRowV<NCH> + (16 * dt + 4 * (li & 3)) * 2;
+}
+// Key (inside its tile) of accumulator element e of subtile s in lane group lg.
+__device__ __forceinline__ int acc_key(int lg, int s, int e) { return 16 * s + 4 * lg + e; }
+// The first of the two keys whose impact totals row16_sum8 leaves in lane
+// (li, lg) of a group (elements 2(li/4), 2(li/4) + 1 of its eight).
+__device__ __forceinline__ int imp_key(int li, int lg) { return 4 * lg + 2 * (li >> 2) + 12 * (li >> 3); }
 
 // A key tile's descriptor held in scalar registers (passed by value so it is
 // never demoted to scratch memory).
@@ -81,44 +115,21 @@ struct Staged {
 
 // A thread's fixed part of the staging, computed once. Thread t moves the
 // chunks t + i NT: with NT a multiple of NCH its column chunk ch = t % NCH is
-// the same for every i and its key advances by KS = NT / NCH rows per i. The
-// XOR swizzle of row k0 + i KS is then the swizzle of the thread's first
-// row k0 XOR a value that depends on i alone (kconst / vconst, checked at
-// compile time for every thread), so the LDS byte offset of chunk i is one
-// of at most four per-thread bases (K; two for V) plus the compile-time
-// i KS ROW: no per-chunk LDS address arithmetic beyond the instructions'
-// immediate offsets. The global side clamps the key to the tile's last
-// valid one (a min and a shift-or per chunk).
+// the same for every i and its key advances by KS = NT / NCH rows per i, so
+// the LDS byte offset of chunk i is the thread's first offset plus the
+// compile-time i KS times the row stride. The global side clamps the key to
+// the tile's last valid one (a min and a shift-or per chunk).
 // WITH_V stages K then V of one tile; otherwise K alone.
 template <int NCH, bool WITH_V, int NT>
 struct Stager {
     using S = Staged<NCH, WITH_V, NT>;
-    static constexpr int ROW = NCH * 16;
     static constexpr int KS = NT / NCH;
-    static_assert(NT % NCH == 0 && KS % 4 == 0, "a thread keeps its column chunk and its key's low two bits");
+    static_assert(NT % NCH == 0, "a thread keeps its column chunk");
     static constexpr bool is_v(int i) { return WITH_V && i * NT >= S::CH; }
     static constexpr int rel(int i) { return is_v(i) ? i - S::CH / NT : i; }   // chunk step inside K or V
-    static constexpr int kconst(int r) { return kswz<NCH>(r * KS) ^ kswz<NCH>(0); }
-    static constexpr int vconst(int r) { return vswz<NCH>(r * KS) ^ vswz<NCH>(0); }
-    static constexpr int kslot(int r) { return kconst(r) >> 2; }   // 0 .. 3
-    static constexpr int vslot(int r) { return vconst(r) >> 3; }   // 0 .. 1
-    static constexpr bool split_ok()
-    {
-        for (int t = 0; t < NT; ++t)
-            for (int r = 0; r * NT < S::CH; ++r) {
-                const int k0 = t / NCH;
-                if (kswz<NCH>(k0 + r * KS) != (kswz<NCH>(k0) ^ kconst(r)) ||
-                    vswz<NCH>(k0 + r * KS) != (vswz<NCH>(k0) ^ vconst(r)) || (kconst(r) & 3) != 0 ||
-                    kslot(r) > 3 || (vconst(r) & 7) != 0 || vslot(r) > 1)
-                    return false;
-            }
-        return true;
-    }
-    static_assert(split_ok(), "swizzle of a thread's rows = its first row's XOR a per-step constant");
     static constexpr bool all_valid = S::TOTAL % NT == 0;
 
-    uint32_t kb[4];     // LDS byte offsets of the thread's K chunks, per kslot
-    uint32_t vb[2];     // the same in a V tile, per vslot
+    uint32_t kb, vb;    // LDS byte offsets of the thread's first K and V chunks
     bool last_ok;       // chunk PER - 1 exists (always, when all_valid)
     int k0, ch;
 
@@ -126,18 +137,13 @@ struct Stager {
     {
         k0 = t / NCH;
         ch = t % NCH;
-        const int uk = ch ^ kswz<NCH>(k0), uv = ch ^ vswz<NCH>(k0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            kb[q] = (uint32_t)(k0 * ROW + ((uk ^ (q << 2)) << 4));
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            vb[q] = (uint32_t)(k0 * ROW + ((uv ^ (q << 3)) << 4));
+        kb = (uint32_t)(k0 * kRowK<NCH> + ch * 16);
+        vb = (uint32_t)(k0 * kRowV<NCH> + ch * 16);
         last_ok = all_valid || t + (S::PER - 1) * NT < S::TOTAL;
     }
     __device__ __forceinline__ bool has(int i) const { return i < S::PER - 1 || last_ok; }
-    __device__ __forceinline__ uint32_t klds(int i) const { return kb[kslot(rel(i))] + (uint32_t)(rel(i) * KS * ROW); }
-    __device__ __forceinline__ uint32_t vlds(int i) const { return vb[vslot(rel(i))] + (uint32_t)(rel(i) * KS * ROW); }
+    __device__ __forceinline__ uint32_t klds(int i) const { return kb + (uint32_t)(rel(i) * KS * kRowK<NCH>); }
+    __device__ __forceinline__ uint32_t vlds(int i) const { return vb + (uint32_t)(rel(i) * KS * kRowV<NCH>); }
 
     // Row `key` of KV head g of the tile's segment starts g * seg_len rows past
     // the tile's base; keys past n_valid repeat the last real key (masked
@@ -226,7 +232,6 @@ struct StagerQ8 {
     static constexpr int CPR = D / 16;          // 16-byte code chunks per row
     static constexpr int CH = kKeyTile * CPR;   // code chunks per tile
     static constexpr int NCH = D / 8;           // 16-byte bf16 chunks per row
-    static constexpr int ROW = 2 * D;
     static_assert(CH <= NT, "one code chunk per thread");
     using S = StagedQ8<D, WITH_V, NT>;
     bool active;
@@ -239,10 +244,10 @@ struct StagerQ8 {
         key = t / CPR;
         c16 = t % CPR;
         const int ch0 = 2 * c16, ch1 = 2 * c16 + 1;
-        lk0 = (uint32_t)(key * ROW + ((ch0 ^ kswz<NCH>(key)) << 4));
-        lk1 = (uint32_t)(key * ROW + ((ch1 ^ kswz<NCH>(key)) << 4));
-        lv0 = (uint32_t)(key * ROW + ((ch0 ^ vswz<NCH>(key)) << 4));
-        lv1 = (uint32_t)(key * ROW + ((ch1 ^ vswz<NCH>(key)) << 4));
+        lk0 = (uint32_t)(key * kRowK<NCH> + ch0 * 16);
+        lk1 = (uint32_t)(key * kRowK<NCH> + ch1 * 16);
+        lv0 = (uint32_t)(key * kRowV<NCH> + ch0 * 16);
+        lv1 = (uint32_t)(key * kRowV<NCH> + ch1 * 16);
     }
 
     // Keys past n_valid repeat the last real key (masked later).
@@ -353,9 +358,9 @@ __device__ __forceinline__ void mask_scores(Spair &s, int lim, int lg)
 {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        if (8 * lg + e > lim)
+        if (acc_key(lg, 0, e) > lim)
             s.s0[e] = -INFINITY;
-        if (8 * lg + 4 + e > lim)
+        if (acc_key(lg, 1, e) > lim)
             s.s1[e] = -INFINITY;
     }
 }

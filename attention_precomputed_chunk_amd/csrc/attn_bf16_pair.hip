@@ -52,12 +52,11 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
     constexpr int KS = D / 32;                 // MFMA k-steps along d
     constexpr int DT = D / 16;                 // output d tiles
     constexpr int NCH = D / 8;                 // 16-byte chunks per row
-    constexpr int ROW = 2 * D;                 // LDS bytes per K or V row
-    constexpr int TILE = kKeyTile * ROW;       // LDS bytes per K (or V) tile
     static_assert(kKeyTile == 32 && RT % 2 == 0, "tile geometry");
 
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_v[3][TILE];
+    // Sweep 1 stages K tiles into both arrays (a V tile is the larger).
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][kTileK<NCH>];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_v[3][kTileV<NCH>];
     __shared__ __attribute__((aligned(16))) bf16x8 lds_p[2][kWaves][RT][64];
     __shared__ __attribute__((aligned(16))) float lds_imp[2][kWaves][kKeyTile];
     __shared__ float lds_lse[LSE_IN ? 1 : kWaves * RT * kRowTile];
@@ -78,14 +77,8 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
         return;
 
     // Per-lane LDS byte offsets inside a tile.
-    const int kkey0 = 8 * (li >> 2) + (li & 3);          // A row li of subtile 0 (subtile 1: +4)
-    const int ksw = kswz<NCH>(kkey0);                     // same for kkey0 + 4
-    auto k_off = [&](int sub, int ks) { return (kkey0 + 4 * sub) * ROW + (((4 * ks + lg) ^ ksw) << 4); };
-    auto v_off = [&](int dt, int r) {
-        const int key = 8 * lg + 4 * r + (li >> 2);
-        const int d = 16 * dt + 4 * (li & 3);
-        return key * ROW + (((d >> 3) ^ vswz<NCH>(key)) << 4) + (d & 7) * 2;
-    };
+    auto k_off = [&](int sub, int ks) { return k_frag_off<NCH>(li, lg, sub, ks); };
+    auto v_off = [&](int dt, int r) { return v_frag_off<NCH>(li, lg, r, dt); };
     auto desc = [&](int tt) { return load_tile(pr.tiles, kt0 + min(tt, n_kt - 1), lane); };
     auto min_pos = [&](int t0) { return pr.pos0 + (t0 * kRowTile) / G; };
 
@@ -262,7 +255,7 @@ __global__ void __launch_bounds__(kWsThreads) attn_bf16_pair_kernel(const AttnAr
             float i0, i1;
             row16_sum8(imp, li, i0, i1);
             if ((li & 3) == 0)
-                *reinterpret_cast<float2 *>(&lds_imp[buf][pair][8 * lg + 2 * (li >> 2)]) = make_float2(i0, i1);
+                *reinterpret_cast<float2 *>(&lds_imp[buf][pair][imp_key(li, lg)]) = make_float2(i0, i1);
         };
         TileSR cur = to_sr(desc(0));
         uint32_t craw = desc(1);

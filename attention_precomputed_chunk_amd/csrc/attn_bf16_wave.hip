@@ -53,9 +53,9 @@ constexpr int kSideSlack = 2;
 // last wave of a partial block holds fewer).
 template <int D, int RT, int RTW, int SIDE, bool CROSS, bool KV8, bool LSE_IN>
 __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
-                                          unsigned char (*lds_k)[kKeyTile * 2 * D],
-                                          unsigned char (*lds_v)[kKeyTile * 2 * D],
-                                          unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16],
+                                          unsigned char (*lds_k)[kTileK<D / 8>],
+                                          unsigned char (*lds_v)[kTileV<D / 8>],
+                                          unsigned char (*lds_kl)[KV8 ? kTileK<D / 8> : 16],
                                           float (*lds_imp)[kWaves][kKeyTile])
 {
     static_assert(SIDE == kSideShare || (LSE_IN && !KV8), "side-work split: bf16, pass 1 on its own");
@@ -66,7 +66,6 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
     constexpr int KS = D / 32;                 // MFMA k-steps along d
     constexpr int DT = D / 16;                 // output d tiles
     constexpr int NCH = D / 8;                 // 16-byte chunks per row
-    constexpr int ROW = 2 * D;                 // LDS bytes per K or V row
     static_assert(kKeyTile == 32, "tile geometry");
     // bf16 segments are staged as they are; 8-bit ones are widened on the way
     // (K into a bf16 hi/lo pair of tiles, V into one bf16 tile)
@@ -117,14 +116,8 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
     }
 
     // Per-lane LDS byte offsets inside a tile.
-    const int kkey0 = 8 * (li >> 2) + (li & 3);          // A row li of subtile 0 (subtile 1: +4)
-    const int ksw = kswz<NCH>(kkey0);                     // same for kkey0 + 4
-    auto k_off = [&](int sub, int ks) { return (kkey0 + 4 * sub) * ROW + (((4 * ks + lg) ^ ksw) << 4); };
-    auto v_off = [&](int dt, int r) {
-        const int key = 8 * lg + 4 * r + (li >> 2);
-        const int d = 16 * dt + 4 * (li & 3);
-        return key * ROW + (((d >> 3) ^ vswz<NCH>(key)) << 4) + (d & 7) * 2;
-    };
+    auto k_off = [&](int sub, int ks) { return k_frag_off<NCH>(li, lg, sub, ks); };
+    auto v_off = [&](int dt, int r) { return v_frag_off<NCH>(li, lg, r, dt); };
 
     const int n_kt = it.n_ktiles;   // key tiles kt0 .. kt0 + n_kt - 1 of the problem's list
     const int kt0 = it.kt_begin;
@@ -162,9 +155,9 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
                 const int lim = min(kt.n_valid - 1, row_pos[rt] - kt.key0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (8 * lg + e > lim)
+                    if (acc_key(lg, 0, e) > lim)
                         s0[e] = -INFINITY;
-                    if (8 * lg + 4 + e > lim)
+                    if (acc_key(lg, 1, e) > lim)
                         s1[e] = -INFINITY;
                 }
             }
@@ -337,9 +330,9 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
                 const int lim = min(kt.n_valid - 1, row_pos[rt] - kt.key0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (8 * lg + e > lim)
+                    if (acc_key(lg, 0, e) > lim)
                         s0[e] = -INFINITY;
-                    if (8 * lg + 4 + e > lim)
+                    if (acc_key(lg, 1, e) > lim)
                         s1[e] = -INFINITY;
                 }
             }
@@ -371,7 +364,7 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
         float i0, i1;
         row16_sum8(imp, li, i0, i1);
         if ((li & 3) == 0)
-            *reinterpret_cast<float2 *>(&lds_imp[buf][wave][8 * lg + 2 * (li >> 2)]) = make_float2(i0, i1);
+            *reinterpret_cast<float2 *>(&lds_imp[buf][wave][imp_key(li, lg)]) = make_float2(i0, i1);
     };
 
     // Unmasked tiles, software-pipelined over the row tiles: stage rt issues
@@ -468,7 +461,7 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
         float i0, i1;
         row16_sum8(imp, li, i0, i1);
         if ((li & 3) == 0)
-            *reinterpret_cast<float2 *>(&lds_imp[buf][wave][8 * lg + 2 * (li >> 2)]) = make_float2(i0, i1);
+            *reinterpret_cast<float2 *>(&lds_imp[buf][wave][imp_key(li, lg)]) = make_float2(i0, i1);
     };
 
     if (n_kt > 0) {
@@ -555,10 +548,9 @@ __device__ __forceinline__ void wave_body(const AttnArgs &a, const ItemDesc &it,
 template <int D, int RT, bool CROSS, bool KV8, bool LSE_IN>
 __global__ void __launch_bounds__(kThreads, 1) attn_bf16_wave_kernel(const AttnArgs a)
 {
-    constexpr int TILE = kKeyTile * 2 * D;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? TILE : 16];   // K lo (8-bit)
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][kTileK<D / 8>];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][kTileV<D / 8>];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 2 : 1][KV8 ? kTileK<D / 8> : 16];   // K lo (8-bit)
     __shared__ float lds_imp[2][kWaves][kKeyTile];
     const ItemDesc it = a.items[blockIdx.x];
     if (it.n_rowtiles == 0)

@@ -35,13 +35,12 @@ namespace crkv {
 // The wave's row tiles are first .. first + R - 1 of the block.
 template <int D, int R, bool KV8, bool SPLIT, typename Stg>
 __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr, const Stg &stg,
-                                         unsigned char (*lds_k)[kKeyTile * 2 * D],
-                                         unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int first, int lane,
+                                         unsigned char (*lds_k)[kTileK<D / 8>],
+                                         unsigned char (*lds_kl)[KV8 ? kTileK<D / 8> : 16], int first, int lane,
                                          int srank)
 {
     constexpr int KS = D / 32;
     constexpr int NCH = D / 8;
-    constexpr int ROW = 2 * D;
     constexpr int RR = R > 0 ? R : 1;
     const int li = lane & 15, lg = lane >> 4;
     const int G = a.G;
@@ -60,9 +59,7 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
     }
     const int wave_min_pos = pr.pos0 + ((it.tile_begin + first) * kRowTile) / G;
 
-    const int kkey0 = 8 * (li >> 2) + (li & 3);
-    const int ksw = kswz<NCH>(kkey0);
-    auto k_off = [&](int sub, int ks) { return (kkey0 + 4 * sub) * ROW + (((4 * ks + lg) ^ ksw) << 4); };
+    auto k_off = [&](int sub, int ks) { return k_frag_off<NCH>(li, lg, sub, ks); };
     auto load_kf = [&](int buf, bf16x8 (&kf)[2][KS], bf16x8 (&kfl)[KV8 ? 2 : 1][KS]) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -100,9 +97,9 @@ __device__ __forceinline__ void lse_body(const AttnArgs &a, const ItemDesc &it, 
                 const int lim = min(kt.n_valid - 1, row_pos[i] - kt.key0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (8 * lg + e > lim)
+                    if (acc_key(lg, 0, e) > lim)
                         s0[e] = -INFINITY;
-                    if (8 * lg + 4 + e > lim)
+                    if (acc_key(lg, 1, e) > lim)
                         s1[e] = -INFINITY;
                 }
             }
@@ -243,8 +240,8 @@ __device__ __forceinline__ int lse_rows(int n, int wave)
 // the busier SIMDs only score.
 template <int D, bool KV8, bool SPLIT>
 __device__ __forceinline__ void lse_dispatch(const AttnArgs &a, const ItemDesc &it, const ProbDesc &pr,
-                                             unsigned char (*lds_k)[kKeyTile * 2 * D],
-                                             unsigned char (*lds_kl)[KV8 ? kKeyTile * 2 * D : 16], int wave,
+                                             unsigned char (*lds_k)[kTileK<D / 8>],
+                                             unsigned char (*lds_kl)[KV8 ? kTileK<D / 8> : 16], int wave,
                                              int lane, int srank)
 {
     constexpr int NCH = D / 8;
@@ -267,9 +264,8 @@ __device__ __forceinline__ void lse_dispatch(const AttnArgs &a, const ItemDesc &
 template <int D, bool KV8>
 __global__ void __launch_bounds__(kLseWaves * 64, 1) attn_lse_kernel(const AttnArgs a)
 {
-    constexpr int TILE = kKeyTile * 2 * D;
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[4][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 4 : 1][KV8 ? TILE : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[4][kTileK<D / 8>];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_kl[KV8 ? 4 : 1][KV8 ? kTileK<D / 8> : 16];
 
     const ItemDesc it = a.items[blockIdx.x];
     if (it.n_rowtiles == 0 || it.n_ktiles == 0)
