@@ -353,7 +353,10 @@ __device__ __forceinline__ Spair scores(const bf16x8 (&kf)[2][KS], const bf16x8 
 }
 
 // Scores past the tile's valid keys or past the row's causal limit (`lim`,
-// relative to the tile's first key) become -inf.
+// relative to the tile's first key) become -inf. mask_scores takes the
+// attention kernels' key order (acc_key); mask_scores_decode the decode
+// kernels', whose A rows of subtile s are keys 8(i/4) + 4s + i%4, so that
+// element e of subtile s in lane group lg is key 8 lg + 4 s + e.
 __device__ __forceinline__ void mask_scores(Spair &s, int lim, int lg)
 {
 #pragma unroll
@@ -361,6 +364,16 @@ __device__ __forceinline__ void mask_scores(Spair &s, int lim, int lg)
         if (acc_key(lg, 0, e) > lim)
             s.s0[e] = -INFINITY;
         if (acc_key(lg, 1, e) > lim)
+            s.s1[e] = -INFINITY;
+    }
+}
+__device__ __forceinline__ void mask_scores_decode(Spair &s, int lim, int lg)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (8 * lg + e > lim)
+            s.s0[e] = -INFINITY;
+        if (8 * lg + 4 + e > lim)
             s.s1[e] = -INFINITY;
     }
 }

@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(kDecodeThreads, 2) decode_split_kernel(const D
 
             Spair sc = scores<KS>(fc.k, qf);
             if (cur.n_valid < kKeyTile)
-                mask_scores(sc, cur.n_valid - 1, lg);
+                mask_scores_decode(sc, cur.n_valid - 1, lg);
             float tmax = fmaxf(fmaxf(fmaxf(sc.s0[0], sc.s0[1]), fmaxf(sc.s0[2], sc.s0[3])),
                                fmaxf(fmaxf(sc.s1[0], sc.s1[1]), fmaxf(sc.s1[2], sc.s1[3])));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));

@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(kQ8DecodeThreads, 2) decode_q8_split_kernel(co
             sc.s0 += sl.s0;
             sc.s1 += sl.s1;
             if (cur.n_valid < kKeyTile)
-                mask_scores(sc, cur.n_valid - 1, lg);
+                mask_scores_decode(sc, cur.n_valid - 1, lg);
             float tmax = fmaxf(fmaxf(fmaxf(sc.s0[0], sc.s0[1]), fmaxf(sc.s0[2], sc.s0[3])),
                                fmaxf(fmaxf(sc.s1[0], sc.s1[1]), fmaxf(sc.s1[2], sc.s1[3])));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
