@@ -178,7 +178,7 @@ struct Stager {
     }
 
     // A K-only stager moving the same chunks of the tile's V instead (into
-    // V's swizzled slots).
+    // a V tile, whose rows have the V stride).
     __device__ __forceinline__ S load_v(TileSR kt, int kv_head) const
     {
         static_assert(!WITH_V, "K-only stager");
